@@ -1,0 +1,83 @@
+"""Pins for the oracle's PSA rearrangements and block: torch view/permute
+(a different formulation of the same index maps), a tiny case readable by eye,
+the pack/merge consistency on the V channels, and the V-split trick checked
+against one attention with the full value width."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+
+def _qkv(b, nh, kd, h, w, dtype=torch.float16, seed=0):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(b, nh * 4 * kd, h, w, generator=g).to(dtype)
+
+
+def _bits(t):
+    if isinstance(t, np.ndarray):
+        return t.view(np.int16)
+    return t.contiguous().view(torch.int16).numpy()
+
+
+@pytest.mark.parametrize("b,nh,kd,h,w", [(1, 1, 1, 1, 2), (2, 3, 4, 5, 3), (16, 4, 32, 20, 20)])
+def test_pack_matches_torch_permute(b, nh, kd, h, w):
+    x = _qkv(b, nh, kd, h, w)
+    got = oracle.psa_pack(x, nh, kd)
+    want = x.view(b, nh, 4, kd, h * w).permute(2, 0, 1, 4, 3).reshape(4, b * nh, h * w, kd)
+    assert np.array_equal(_bits(got), _bits(want))
+
+
+def test_pack_tiny_by_eye():
+    # one batch, one head, key_dim 1, two pixels: channels are (Q, K, V_lo, V_hi)
+    x = torch.tensor([[[[1.0, 2.0]], [[3.0, 4.0]], [[5.0, 6.0]], [[7.0, 8.0]]]], dtype=torch.float16)
+    got = oracle.psa_pack(x, 1, 1)
+    want = torch.tensor([[[[1.0], [2.0]]], [[[3.0], [4.0]]], [[[5.0], [6.0]]], [[[7.0], [8.0]]]],
+                        dtype=torch.float16)
+    assert got.shape == (4, 1, 2, 1)
+    assert np.array_equal(_bits(got), _bits(want))
+
+
+@pytest.mark.parametrize("b,nh,kd,h,w", [(1, 1, 2, 1, 3), (2, 3, 4, 5, 3), (16, 4, 32, 20, 20)])
+def test_merge_matches_torch_permute(b, nh, kd, h, w):
+    g = torch.Generator().manual_seed(1)
+    lo = torch.randn(b * nh, h * w, kd, generator=g).to(torch.bfloat16)
+    hi = torch.randn(b * nh, h * w, kd, generator=g).to(torch.bfloat16)
+    got = oracle.psa_merge(lo, hi, b, nh, kd, h, w)
+    both = torch.stack([lo, hi], 0).view(2, b, nh, h * w, kd)  # [2, B, nh, N, kd]
+    want = both.permute(1, 2, 0, 4, 3).reshape(b, nh * 2 * kd, h, w)
+    assert np.array_equal(_bits(got), _bits(want))
+
+
+def test_pack_then_merge_recovers_value_channels():
+    b, nh, kd, h, w = 2, 3, 4, 3, 5
+    x = _qkv(b, nh, kd, h, w, seed=3)
+    packed = oracle.psa_pack(x, nh, kd)
+    merged = oracle.psa_merge(packed[2], packed[3], b, nh, kd, h, w)
+    xb = _bits(x).reshape(b, nh, 4 * kd, h, w)
+    want = xb[:, :, 2 * kd:, :, :].reshape(b, nh * 2 * kd, h, w)
+    assert np.array_equal(_bits(merged), want)
+
+
+def test_split_trick_equals_full_value_width():
+    b, nh, kd, h, w = 2, 2, 4, 3, 4
+    x = _qkv(b, nh, kd, h, w, seed=4).double()
+    out = oracle.psa_block(x, nh, kd)
+    packed = oracle.psa_pack(x, nh, kd)
+    v_full = np.concatenate([packed[2], packed[3]], axis=-1)  # dv = 2*kd
+    o_full, _ = oracle.attention_fwd(packed[0], packed[1], v_full, 1 / np.sqrt(kd))
+    ref = oracle.psa_merge(np.ascontiguousarray(o_full[..., :kd]), np.ascontiguousarray(o_full[..., kd:]),
+                           b, nh, kd, h, w)
+    np.testing.assert_allclose(out, ref, atol=1e-14)
+
+
+def test_block_matches_torch_composite():
+    b, nh, kd, h, w = 2, 2, 8, 4, 5
+    x = _qkv(b, nh, kd, h, w, seed=5).double()
+    out = oracle.psa_block(x, nh, kd)
+    t = x.view(b, nh, 4, kd, h * w).transpose(-1, -2)  # [B, nh, 4, N, kd]
+    qt, kt = t[:, :, 0], t[:, :, 1]
+    vt = torch.cat([t[:, :, 2], t[:, :, 3]], dim=-1)    # [B, nh, N, 2kd]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=kd ** -0.5)
+    want = o.transpose(-1, -2).reshape(b, nh * 2 * kd, h, w)
+    np.testing.assert_allclose(out, want.numpy(), atol=1e-12)
