@@ -1,0 +1,198 @@
+"""MI355X-native exact attention (FlashAttention-2 style) and the PSA
+pack/merge rearrangements, behind the C ABI of ``libfa2mi.so``
+(``include/fa2mi.h``).
+
+This module only marshals arguments: it checks tensors, allocates outputs with
+torch on the inputs' device, and calls the C entry point of the same name with
+raw device pointers and the current torch stream. Every step of the
+computation runs in the HIP kernels; there is no fallback of any kind, and
+every function raises if the library is missing or the tensors are not on a
+GPU.
+
+Entry points (same names as the C ABI):
+  fa2_fwd, fa2_bwd_delta, fa2_bwd_dq, fa2_bwd_dkdv, psa_pack_qkv, psa_merge_attn
+Compositions of them:
+  attention_fwd (= fa2_fwd), attention_bwd (delta -> dkdv -> dq),
+  psa_block (pack -> fa2_fwd on V_lo -> fa2_fwd on V_hi -> merge)
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+from ._lib import FA2_BF16, FA2_F16, FA2_F32, Fa2Error, library_path, load  # noqa: F401
+
+__all__ = [
+    "fa2_fwd", "fa2_bwd_delta", "fa2_bwd_dq", "fa2_bwd_dkdv", "psa_pack_qkv", "psa_merge_attn",
+    "attention_fwd", "attention_bwd", "psa_block", "Fa2Error", "load", "library_path",
+]
+
+_DT = {torch.float32: FA2_F32, torch.float16: FA2_F16, torch.bfloat16: FA2_BF16}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32, float16 or bfloat16") from None
+
+
+def _check(name: str, t: torch.Tensor, dtype=None, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _scale(scale, head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim) if scale is None else float(scale)
+
+
+def fa2_fwd(q, k, v, scale=None, o=None, lse=None):
+    """Forward: returns (o [bh,n_q,d] in q's dtype, lse [bh,n_q] float32)."""
+    _check("q", q)
+    bh, n_q, d = q.shape
+    n_k = k.shape[1]
+    dev = q.device
+    _check("k", k, q.dtype, (bh, n_k, d), dev)
+    _check("v", v, q.dtype, (bh, n_k, d), dev)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((bh, n_q), dtype=torch.float32, device=dev)
+    _check("o", o, q.dtype, q.shape, dev)
+    _check("lse", lse, torch.float32, (bh, n_q), dev)
+    _lib.call("fa2_fwd", _dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+              lse.data_ptr(), bh, n_q, n_k, d, _scale(scale, d), _stream(dev))
+    return o, lse
+
+
+def fa2_bwd_delta(o, do, delta=None):
+    """delta [bh,n_q] float32 = rowsum(o * do)."""
+    _check("o", o)
+    bh, n_q, d = o.shape
+    _check("do", do, o.dtype, o.shape, o.device)
+    if delta is None:
+        delta = torch.empty((bh, n_q), dtype=torch.float32, device=o.device)
+    _check("delta", delta, torch.float32, (bh, n_q), o.device)
+    _lib.call("fa2_bwd_delta", _dtype_code(o), o.data_ptr(), do.data_ptr(), delta.data_ptr(), bh, n_q, d,
+              _stream(o.device))
+    return delta
+
+
+def _bwd_checks(q, k, v, do, lse, delta):
+    _check("q", q)
+    bh, n_q, d = q.shape
+    n_k = k.shape[1]
+    dev = q.device
+    _check("k", k, q.dtype, (bh, n_k, d), dev)
+    _check("v", v, q.dtype, (bh, n_k, d), dev)
+    _check("do", do, q.dtype, q.shape, dev)
+    _check("lse", lse, torch.float32, (bh, n_q), dev)
+    _check("delta", delta, torch.float32, (bh, n_q), dev)
+    return bh, n_q, n_k, d, dev
+
+
+def fa2_bwd_dq(q, k, v, do, lse, delta, scale=None, dq=None):
+    """dq [bh,n_q,d] from the saved lse and delta."""
+    bh, n_q, n_k, d, dev = _bwd_checks(q, k, v, do, lse, delta)
+    if dq is None:
+        dq = torch.empty_like(q)
+    _check("dq", dq, q.dtype, q.shape, dev)
+    _lib.call("fa2_bwd_dq", _dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
+              lse.data_ptr(), delta.data_ptr(), dq.data_ptr(), bh, n_q, n_k, d, _scale(scale, d), _stream(dev))
+    return dq
+
+
+def fa2_bwd_dkdv(q, k, v, do, lse, delta, scale=None, dk=None, dv=None):
+    """(dk, dv) [bh,n_k,d] from the saved lse and delta."""
+    bh, n_q, n_k, d, dev = _bwd_checks(q, k, v, do, lse, delta)
+    if dk is None:
+        dk = torch.empty_like(k)
+    if dv is None:
+        dv = torch.empty_like(v)
+    _check("dk", dk, q.dtype, k.shape, dev)
+    _check("dv", dv, q.dtype, v.shape, dev)
+    _lib.call("fa2_bwd_dkdv", _dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
+              lse.data_ptr(), delta.data_ptr(), dk.data_ptr(), dv.data_ptr(), bh, n_q, n_k, d,
+              _scale(scale, d), _stream(dev))
+    return dk, dv
+
+
+def attention_fwd(q, k, v, scale=None):
+    """(o, lse) of softmax(scale q k^T) v."""
+    return fa2_fwd(q, k, v, scale)
+
+
+def attention_bwd(q, k, v, o, do, lse, scale=None):
+    """(dq, dk, dv) given the forward's o and lse and the output gradient do."""
+    delta = fa2_bwd_delta(o, do)
+    dk, dv = fa2_bwd_dkdv(q, k, v, do, lse, delta, scale)
+    dq = fa2_bwd_dq(q, k, v, do, lse, delta, scale)
+    return dq, dk, dv
+
+
+def psa_pack_qkv(qkv, num_heads: int, key_dim: int, packed=None):
+    """qkv [B, nh*4*kd, H, W] -> packed [4, B*nh, H*W, kd] (Q, K, V_lo, V_hi)."""
+    _check("qkv", qkv)
+    b, ch, h, w = qkv.shape
+    if ch != num_heads * 4 * key_dim:
+        raise ValueError(f"qkv has {ch} channels, expected num_heads*4*key_dim = {num_heads * 4 * key_dim}")
+    if packed is None:
+        packed = torch.empty((4, b * num_heads, h * w, key_dim), dtype=qkv.dtype, device=qkv.device)
+    _check("packed", packed, qkv.dtype, (4, b * num_heads, h * w, key_dim), qkv.device)
+    _lib.call("psa_pack_qkv", _dtype_code(qkv), qkv.data_ptr(), packed.data_ptr(), b, num_heads, key_dim, h, w,
+              _stream(qkv.device))
+    return packed
+
+
+def psa_merge_attn(o_lo, o_hi, batch: int, num_heads: int, h: int, w: int, out=None):
+    """o_lo, o_hi [B*nh, H*W, kd] -> out [B, nh*2*kd, H, W]."""
+    _check("o_lo", o_lo)
+    bh, n, kd = o_lo.shape
+    if bh != batch * num_heads or n != h * w:
+        raise ValueError("o_lo shape does not match batch*num_heads x h*w")
+    _check("o_hi", o_hi, o_lo.dtype, o_lo.shape, o_lo.device)
+    if out is None:
+        out = torch.empty((batch, num_heads * 2 * kd, h, w), dtype=o_lo.dtype, device=o_lo.device)
+    _check("out", out, o_lo.dtype, (batch, num_heads * 2 * kd, h, w), o_lo.device)
+    _lib.call("psa_merge_attn", _dtype_code(o_lo), o_lo.data_ptr(), o_hi.data_ptr(), out.data_ptr(), batch,
+              num_heads, kd, h, w, _stream(o_lo.device))
+    return out
+
+
+def psa_block(qkv, num_heads: int, key_dim: int, workspace: dict | None = None):
+    """PSA attention block: pack -> fa2_fwd(Q, K, V_lo) -> fa2_fwd(Q, K, V_hi)
+    -> merge, at scale 1/sqrt(key_dim). ``workspace`` (optional dict) keeps
+    the intermediate buffers between calls of the same shape."""
+    b, _, h, w = qkv.shape
+    ws = workspace if workspace is not None else {}
+    shape_key = (tuple(qkv.shape), qkv.dtype, qkv.device, num_heads, key_dim)
+    if ws.get("key") != shape_key:
+        bh, n = b * num_heads, h * w
+        ws.clear()
+        ws["key"] = shape_key
+        ws["packed"] = torch.empty((4, bh, n, key_dim), dtype=qkv.dtype, device=qkv.device)
+        ws["o"] = torch.empty((2, bh, n, key_dim), dtype=qkv.dtype, device=qkv.device)
+        ws["lse"] = torch.empty((bh, n), dtype=torch.float32, device=qkv.device)
+        ws["out"] = torch.empty((b, num_heads * 2 * key_dim, h, w), dtype=qkv.dtype, device=qkv.device)
+    packed, o, lse = ws["packed"], ws["o"], ws["lse"]
+    psa_pack_qkv(qkv, num_heads, key_dim, packed)
+    scale = 1.0 / math.sqrt(key_dim)
+    fa2_fwd(packed[0], packed[1], packed[2], scale, o[0], lse)
+    fa2_fwd(packed[0], packed[1], packed[3], scale, o[1], lse)
+    return psa_merge_attn(o[0], o[1], b, num_heads, h, w, ws["out"])

@@ -1,0 +1,172 @@
+// C ABI of libfa2mi: argument validation, then one launch on the caller's
+// stream. Validation never touches the HIP runtime, so a rejected call has no
+// side effect at all.
+#include <climits>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/fa2mi.h"
+#include "fa2_launch.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+fa2_status fail(fa2_status st, const char *fn, const char *what) {
+    std::snprintf(g_last_error, sizeof g_last_error, "%s: %s", fn, what);
+    return st;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool good_dtype(fa2_dtype dt) { return dt == FA2_F32 || dt == FA2_F16 || dt == FA2_BF16; }
+
+bool good_dim(int64_t d) { return d == 32 || d == 64 || d == 128; }
+
+#define REQUIRE_PTR(fn, p)                                                          \
+    do {                                                                            \
+        if ((p) == nullptr) return fail(FA2_ERR_INVALID_ARG, fn, #p " is NULL");    \
+        if (!aligned16(p)) return fail(FA2_ERR_INVALID_ARG, fn, #p " is not 16-byte aligned"); \
+    } while (0)
+
+// Common checks of the attention entry points.
+fa2_status check_attn(const char *fn, fa2_dtype dt, int64_t bh, int64_t n_q, int64_t n_k, int32_t head_dim,
+                      float scale, int rows_per_block, int64_t grid_rows) {
+    if (!good_dtype(dt)) return fail(FA2_ERR_INVALID_ARG, fn, "unknown dtype");
+    if (bh <= 0 || n_q <= 0 || n_k <= 0 || head_dim <= 0)
+        return fail(FA2_ERR_INVALID_ARG, fn, "bh, n_q, n_k and head_dim must all be > 0");
+    if (!good_dim(head_dim)) return fail(FA2_ERR_UNSUPPORTED, fn, "head_dim must be 32, 64 or 128");
+    if (n_q * head_dim > INT_MAX || n_k * head_dim > INT_MAX)
+        return fail(FA2_ERR_INVALID_ARG, fn, "n * head_dim exceeds 2^31 - 1 elements per head");
+    if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+        return fail(FA2_ERR_INVALID_ARG, fn, "scale must be finite");
+    const int64_t blocks = (grid_rows + rows_per_block - 1) / rows_per_block;
+    if (bh > INT_MAX / blocks) return fail(FA2_ERR_INVALID_ARG, fn, "grid exceeds 2^31 - 1 workgroups");
+    return FA2_OK;
+}
+
+fa2_status launched(const char *fn, hipError_t e) {
+    if (e != hipSuccess) return fail(FA2_ERR_LAUNCH, fn, hipGetErrorString(e));
+    g_last_error[0] = '\0';
+    return FA2_OK;
+}
+
+fa2_status check_psa(const char *fn, fa2_dtype dt, int32_t batch, int32_t num_heads, int32_t key_dim, int32_t h,
+                     int32_t w) {
+    if (!good_dtype(dt)) return fail(FA2_ERR_INVALID_ARG, fn, "unknown dtype");
+    if (batch <= 0 || num_heads <= 0 || key_dim <= 0 || h <= 0 || w <= 0)
+        return fail(FA2_ERR_INVALID_ARG, fn, "batch, num_heads, key_dim, h and w must all be > 0");
+    if (!good_dim(key_dim)) return fail(FA2_ERR_UNSUPPORTED, fn, "key_dim must be 32, 64 or 128");
+    const int64_t hw = (int64_t)h * w;
+    const int64_t slice_elems = hw * key_dim;
+    if (slice_elems > INT_MAX) return fail(FA2_ERR_INVALID_ARG, fn, "h * w * key_dim exceeds 2^31 - 1");
+    // generous bound on the workgroup count (tiles of >= 8 pixels)
+    const int64_t tiles = (int64_t)batch * num_heads * 4 * ((hw + 7) / 8);
+    if (tiles > INT_MAX) return fail(FA2_ERR_INVALID_ARG, fn, "grid exceeds 2^31 - 1 workgroups");
+    return FA2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fa2_abi_version(void) { return 1; }
+
+const char *fa2_status_str(fa2_status s) {
+    switch (s) {
+        case FA2_OK: return "ok";
+        case FA2_ERR_INVALID_ARG: return "invalid argument";
+        case FA2_ERR_UNSUPPORTED: return "unsupported size";
+        case FA2_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+const char *fa2_last_error(void) { return g_last_error; }
+
+fa2_status fa2_fwd(fa2_dtype dt, const void *q, const void *k, const void *v, void *o, float *lse, int64_t bh,
+                   int64_t n_q, int64_t n_k, int32_t head_dim, float scale, void *stream) {
+    static const char fn[] = "fa2_fwd";
+    fa2_status st = check_attn(fn, dt, bh, n_q, n_k, head_dim, scale, fa2mi::kFwdRowsPerBlock, n_q);
+    if (st != FA2_OK) return st;
+    REQUIRE_PTR(fn, q);
+    REQUIRE_PTR(fn, k);
+    REQUIRE_PTR(fn, v);
+    REQUIRE_PTR(fn, o);
+    REQUIRE_PTR(fn, lse);
+    const fa2mi::AttnShape s{bh, (int)n_q, (int)n_k, head_dim, scale};
+    return launched(fn, fa2mi::launch_fwd((int)dt, q, k, v, o, lse, s, (hipStream_t)stream));
+}
+
+fa2_status fa2_bwd_delta(fa2_dtype dt, const void *o, const void *d_o, float *delta, int64_t bh, int64_t n_q,
+                         int32_t head_dim, void *stream) {
+    static const char fn[] = "fa2_bwd_delta";
+    fa2_status st = check_attn(fn, dt, bh, n_q, 1, head_dim, 1.f, 1 << 30, n_q);
+    if (st != FA2_OK) return st;
+    REQUIRE_PTR(fn, o);
+    REQUIRE_PTR(fn, d_o);
+    REQUIRE_PTR(fn, delta);
+    const int64_t rows = bh * n_q;
+    if (rows / 8 > INT_MAX) return fail(FA2_ERR_INVALID_ARG, fn, "grid exceeds 2^31 - 1 workgroups");
+    return launched(fn, fa2mi::launch_bwd_delta((int)dt, o, d_o, delta, rows, head_dim, (hipStream_t)stream));
+}
+
+fa2_status fa2_bwd_dq(fa2_dtype dt, const void *q, const void *k, const void *v, const void *d_o, const float *lse,
+                      const float *delta, void *dq, int64_t bh, int64_t n_q, int64_t n_k, int32_t head_dim,
+                      float scale, void *stream) {
+    static const char fn[] = "fa2_bwd_dq";
+    fa2_status st = check_attn(fn, dt, bh, n_q, n_k, head_dim, scale, fa2mi::kFwdRowsPerBlock, n_q);
+    if (st != FA2_OK) return st;
+    REQUIRE_PTR(fn, q);
+    REQUIRE_PTR(fn, k);
+    REQUIRE_PTR(fn, v);
+    REQUIRE_PTR(fn, d_o);
+    REQUIRE_PTR(fn, lse);
+    REQUIRE_PTR(fn, delta);
+    REQUIRE_PTR(fn, dq);
+    const fa2mi::AttnShape s{bh, (int)n_q, (int)n_k, head_dim, scale};
+    return launched(fn, fa2mi::launch_bwd_dq((int)dt, q, k, v, d_o, lse, delta, dq, s, (hipStream_t)stream));
+}
+
+fa2_status fa2_bwd_dkdv(fa2_dtype dt, const void *q, const void *k, const void *v, const void *d_o,
+                        const float *lse, const float *delta, void *dk, void *dv, int64_t bh, int64_t n_q,
+                        int64_t n_k, int32_t head_dim, float scale, void *stream) {
+    static const char fn[] = "fa2_bwd_dkdv";
+    fa2_status st = check_attn(fn, dt, bh, n_q, n_k, head_dim, scale, fa2mi::kDkdvKeysPerBlock, n_k);
+    if (st != FA2_OK) return st;
+    REQUIRE_PTR(fn, q);
+    REQUIRE_PTR(fn, k);
+    REQUIRE_PTR(fn, v);
+    REQUIRE_PTR(fn, d_o);
+    REQUIRE_PTR(fn, lse);
+    REQUIRE_PTR(fn, delta);
+    REQUIRE_PTR(fn, dk);
+    REQUIRE_PTR(fn, dv);
+    const fa2mi::AttnShape s{bh, (int)n_q, (int)n_k, head_dim, scale};
+    return launched(fn, fa2mi::launch_bwd_dkdv((int)dt, q, k, v, d_o, lse, delta, dk, dv, s, (hipStream_t)stream));
+}
+
+fa2_status psa_pack_qkv(fa2_dtype dt, const void *qkv, void *packed, int32_t batch, int32_t num_heads,
+                        int32_t key_dim, int32_t h, int32_t w, void *stream) {
+    static const char fn[] = "psa_pack_qkv";
+    fa2_status st = check_psa(fn, dt, batch, num_heads, key_dim, h, w);
+    if (st != FA2_OK) return st;
+    REQUIRE_PTR(fn, qkv);
+    REQUIRE_PTR(fn, packed);
+    const fa2mi::PsaShape s{batch, num_heads, key_dim, h * w};
+    return launched(fn, fa2mi::launch_psa_pack((int)dt, qkv, packed, s, (hipStream_t)stream));
+}
+
+fa2_status psa_merge_attn(fa2_dtype dt, const void *o_lo, const void *o_hi, void *out, int32_t batch,
+                          int32_t num_heads, int32_t key_dim, int32_t h, int32_t w, void *stream) {
+    static const char fn[] = "psa_merge_attn";
+    fa2_status st = check_psa(fn, dt, batch, num_heads, key_dim, h, w);
+    if (st != FA2_OK) return st;
+    REQUIRE_PTR(fn, o_lo);
+    REQUIRE_PTR(fn, o_hi);
+    REQUIRE_PTR(fn, out);
+    const fa2mi::PsaShape s{batch, num_heads, key_dim, h * w};
+    return launched(fn, fa2mi::launch_psa_merge((int)dt, o_lo, o_hi, out, s, (hipStream_t)stream));
+}
+
+}  // extern "C"

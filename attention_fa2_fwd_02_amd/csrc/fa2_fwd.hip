@@ -1,0 +1,221 @@
+// Attention forward (vision-rs flash_attn2.rs, "Forward"; vyre-libs
+// flash_attention_2.rs, tiled builder): O = softmax(scale Q K^T) V and the
+// natural-log LSE per query row, by the online-softmax recurrence over key
+// tiles so the score matrix never leaves registers.
+//
+// Workgroup: WAVES wavefronts, each owning 32 query rows (BR = 32*WAVES rows
+// per workgroup). Per key tile of BC rows:
+//   1. K (row-major) and V (transposed) tiles are staged in LDS; the next
+//      tile is fetched into registers while the current one is computed.
+//   2. S^T = K Q^T on MFMA: one C block per 32 keys; each lane owns one query
+//      (the C column), so a row's max needs one exchange between lane halves.
+//   3. Online softmax in the log2 domain (scale*log2(e) folded into one
+//      multiply, exp2): m' = max(m, rowmax), alpha = 2^(m - m'), P = 2^(S - m'),
+//      l = alpha*l + rowsum(P) (lane-partial sums, combined at the end).
+//   4. O^T = alpha*O^T + V^T P^T on MFMA, P fed from registers as the B operand.
+// Epilogue: O = O^T / l rounded to the element type; LSE = ln2 * (m + log2 l).
+#include "fa2_device.h"
+#include "fa2_launch.h"
+
+namespace fa2mi {
+
+template <Dt DT>
+__device__ __forceinline__ typename Traits<DT>::frag zero_frag() {
+    typename Traits<DT>::frag f;
+    if constexpr (Traits<DT>::KPL == 8) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = static_cast<typename Traits<DT>::elem>(0.f);
+    } else {
+        f = 0.f;
+    }
+    return f;
+}
+
+// Stores the 4 consecutive values c = 4g .. 4g+3 of a C block, scaled by mul,
+// at dst[0..3] in the element type.
+template <Dt DT>
+__device__ __forceinline__ void store4(typename Traits<DT>::elem *dst, const f32x16 &c, int g, float mul) {
+    using elem = typename Traits<DT>::elem;
+    if constexpr (sizeof(elem) == 2) {
+        typename Traits<DT>::half_frag v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = static_cast<elem>(c[4 * g + i] * mul);
+        *reinterpret_cast<typename Traits<DT>::half_frag *>(dst) = v;
+    } else {
+        *reinterpret_cast<float4 *>(dst) =
+            make_float4(c[4 * g] * mul, c[4 * g + 1] * mul, c[4 * g + 2] * mul, c[4 * g + 3] * mul);
+    }
+}
+
+template <Dt DT, int D, int BC, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void fwd_kernel(
+    const typename Traits<DT>::elem *__restrict__ Q, const typename Traits<DT>::elem *__restrict__ K,
+    const typename Traits<DT>::elem *__restrict__ V, typename Traits<DT>::elem *__restrict__ O,
+    float *__restrict__ LSE, int n_q, int n_k, int n_qblocks, int total_blocks, float scale_log2) {
+    using Tr = Traits<DT>;
+    using elem = typename Tr::elem;
+    using frag = typename Tr::frag;
+    constexpr int NT = WAVES * 64;
+    constexpr int BR = 32 * WAVES;
+    constexpr int KPL = Tr::KPL;
+    constexpr int KSTEP = 2 * KPL;
+    constexpr int VEC = vec_elems<DT>();
+    constexpr int LDK = D + VEC;  // row-major K tile stride (16-byte pad)
+    constexpr int LDV = BC + 4;   // transposed V tile stride
+    constexpr int NKB = BC / 32;  // 32-key blocks per tile
+    constexpr int NDB = D / 32;   // 32-row blocks of O^T
+    constexpr int TS = D / KSTEP; // contraction steps over head_dim
+    constexpr int TP = 32 / KSTEP;// contraction steps per 32-key block
+    static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
+
+    __shared__ __attribute__((aligned(16))) elem Ks[BC * LDK];
+    __shared__ __attribute__((aligned(16))) elem Vt[D * LDV];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int h = lane >> 5, col = lane & 31;
+    const int blk = xcd_remap(blockIdx.x, total_blocks);
+    const int bh = blk / n_qblocks, qb = blk % n_qblocks;
+    const int qrow = qb * BR + wave * 32 + col;
+    const int64_t qoff = (int64_t)bh * n_q * D;
+    const int64_t koff = (int64_t)bh * n_k * D;
+
+    frag qf[TS];
+    if (qrow < n_q) {
+        const elem *qp = Q + qoff + (int64_t)qrow * D;
+#pragma unroll
+        for (int t = 0; t < TS; ++t) qf[t] = ld_row_frag<DT>(qp, t, h);
+    } else {
+#pragma unroll
+        for (int t = 0; t < TS; ++t) qf[t] = zero_frag<DT>();
+    }
+
+    f32x16 acc[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) acc[i] = zero16();
+    float m_run = -INFINITY, l_run = 0.f;
+
+    TileStage<DT, BC, D, NT, true> kst;
+    TileStage<DT, BC, D, NT, false> vst;
+    const int ntiles = (n_k + BC - 1) / BC;
+    kst.load(K + koff, n_k, tid);
+    vst.load(V + koff, n_k, tid);
+    kst.template store_rows<LDK>(Ks, tid);
+    vst.template store_transposed<LDV>(Vt, tid);
+    __syncthreads();
+
+    for (int it = 0; it < ntiles; ++it) {
+        const int j0 = it * BC;
+        const bool more = it + 1 < ntiles;
+        if (more) {
+            kst.load(K + koff + (int64_t)(j0 + BC) * D, n_k - j0 - BC, tid);
+            vst.load(V + koff + (int64_t)(j0 + BC) * D, n_k - j0 - BC, tid);
+        }
+
+        // S^T = K Q^T, one 32x32 block per 32 keys
+        f32x16 s[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            s[kb] = zero16();
+            const elem *krow = Ks + (32 * kb + col) * LDK;
+#pragma unroll
+            for (int t = 0; t < TS; ++t) s[kb] = Tr::mfma(ld_row_frag<DT>(krow, t, h), qf[t], s[kb]);
+        }
+
+        // online softmax, log2 domain
+        const int kvalid = n_k - j0;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                float x = s[kb][c] * scale_log2;
+                if (kvalid < BC && 32 * kb + crow(c, h) >= kvalid) x = -INFINITY;
+                s[kb][c] = x;
+                mx = fmaxf(mx, x);
+            }
+        mx = xhalf_max(mx);
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                const float p = __builtin_amdgcn_exp2f(s[kb][c] - m_new);
+                s[kb][c] = p;
+                rs += p;
+            }
+        l_run = l_run * alpha + rs;
+        m_run = m_new;
+
+        // O^T = alpha O^T + V^T P^T
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int c = 0; c < 16; ++c) acc[db][c] *= alpha;
+            const elem *vrow = Vt + (32 * db + col) * LDV;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int t = 0; t < TP; ++t)
+                    acc[db] = Tr::mfma(ld_t_frag<DT>(vrow, kb, t, h), c_to_frag<DT>(s[kb], t), acc[db]);
+        }
+
+        __syncthreads();
+        if (more) {
+            kst.template store_rows<LDK>(Ks, tid);
+            vst.template store_transposed<LDV>(Vt, tid);
+        }
+        __syncthreads();
+    }
+
+    const float l_tot = xhalf_sum(l_run);
+    if (qrow < n_q) {
+        const float inv = 1.f / l_tot;
+        elem *op = O + qoff + (int64_t)qrow * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) store4<DT>(op + 32 * db + 8 * g + 4 * h, acc[db], g, inv);
+        if (h == 0) LSE[(int64_t)bh * n_q + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+    }
+}
+
+template <Dt DT, int D>
+static hipError_t fwd_dispatch(const void *q, const void *k, const void *v, void *o, float *lse,
+                               const AttnShape &s, hipStream_t stream) {
+    using elem = typename Traits<DT>::elem;
+    constexpr int WAVES = 4, BC = 64;
+    constexpr int BR = 32 * WAVES;
+    static_assert(BR == kFwdRowsPerBlock, "row block");
+    const int nqb = (s.n_q + BR - 1) / BR;
+    const int total = (int)(s.bh * nqb);
+    const float scale_log2 = (float)((double)s.scale * 1.4426950408889634);
+    hipLaunchKernelGGL((fwd_kernel<DT, D, BC, WAVES>), dim3(total), dim3(WAVES * 64), 0, stream,
+                       (const elem *)q, (const elem *)k, (const elem *)v, (elem *)o, lse, s.n_q, s.n_k,
+                       nqb, total, scale_log2);
+    return hipGetLastError();
+}
+
+template <Dt DT>
+static hipError_t fwd_by_dim(const void *q, const void *k, const void *v, void *o, float *lse,
+                             const AttnShape &s, hipStream_t stream) {
+    switch (s.head_dim) {
+        case 32: return fwd_dispatch<DT, 32>(q, k, v, o, lse, s, stream);
+        case 64: return fwd_dispatch<DT, 64>(q, k, v, o, lse, s, stream);
+        case 128: return fwd_dispatch<DT, 128>(q, k, v, o, lse, s, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_fwd(int dt, const void *q, const void *k, const void *v, void *o, float *lse,
+                      const AttnShape &s, hipStream_t stream) {
+    switch (dt) {
+        case 0: return fwd_by_dim<Dt::F32>(q, k, v, o, lse, s, stream);
+        case 1: return fwd_by_dim<Dt::F16>(q, k, v, o, lse, s, stream);
+        case 2: return fwd_by_dim<Dt::BF16>(q, k, v, o, lse, s, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace fa2mi

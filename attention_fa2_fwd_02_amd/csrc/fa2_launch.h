@@ -1,0 +1,46 @@
+// Host-side launch interface between the C ABI (fa2_abi.hip) and the kernel
+// translation units. Arguments are already validated when these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa2mi {
+
+struct AttnShape {
+    int64_t bh;
+    int n_q;
+    int n_k;
+    int head_dim;
+    float scale;
+};
+
+// dt: 0 f32, 1 f16, 2 bf16 (the fa2_dtype values).
+hipError_t launch_fwd(int dt, const void *q, const void *k, const void *v, void *o, float *lse,
+                      const AttnShape &s, hipStream_t stream);
+hipError_t launch_bwd_delta(int dt, const void *o, const void *d_o, float *delta, int64_t rows,
+                            int head_dim, hipStream_t stream);
+hipError_t launch_bwd_dq(int dt, const void *q, const void *k, const void *v, const void *d_o,
+                         const float *lse, const float *delta, void *dq, const AttnShape &s,
+                         hipStream_t stream);
+hipError_t launch_bwd_dkdv(int dt, const void *q, const void *k, const void *v, const void *d_o,
+                           const float *lse, const float *delta, void *dk, void *dv,
+                           const AttnShape &s, hipStream_t stream);
+
+struct PsaShape {
+    int batch;
+    int num_heads;
+    int key_dim;
+    int hw;
+};
+
+hipError_t launch_psa_pack(int dt, const void *qkv, void *packed, const PsaShape &s, hipStream_t stream);
+hipError_t launch_psa_merge(int dt, const void *lo, const void *hi, void *out, const PsaShape &s,
+                            hipStream_t stream);
+
+// Query rows per forward / dq workgroup and key rows per dkdv workgroup
+// (the ABI checks that the 1-D grids fit in int32).
+constexpr int kFwdRowsPerBlock = 128;
+constexpr int kDkdvKeysPerBlock = 128;
+
+}  // namespace fa2mi

@@ -1,0 +1,340 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+A step is one pass of the whole path over resident synthetic inputs at the
+LLM shape (BH 512 = 16 x 32 heads, N_q = N_k = 4096, head_dim 128, bf16):
+forward (fa2_fwd: O and LSE), then backward from that O and LSE with a
+synthetic dO (fa2_bwd_delta, fa2_bwd_dkdv, fa2_bwd_dq). `value` is the step's
+algorithmic throughput by the FLOP convention fwd = 4 BH Nq Nk D, bwd = 2.5 x
+fwd. Per-kernel durations come from HIP events recorded around every launch
+on the launch stream inside the timed region.
+
+Legs measured in the same run (not part of `value`): the forward alone at
+that shape, cross-attention (BH 1024, Nq 1024, Nk 8192, D 64, K x 3), the
+backward-config step (BH 256, N 2048, D 128) and the C2PSA block (pack,
+attention twice, merge) warm and with L2/MALL flushed before each call.
+
+The CPU baseline times the fp64 oracle on a bounded sample of the same
+workload (a few heads at full sequence length) on the host cores.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "attention fwd/bwd TFLOP/s + % bf16 MFMA peak; PSA block fwd us/call"
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-legs", action="store_true", help="skip the other-shape legs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=0, help="oracle sample heads (0: one per thread)")
+    return ap.parse_args()
+
+
+class KernelTimer:
+    """HIP events around each launch on the launch stream; sums per name."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pending = []
+        self.total = {}
+        self.count = {}
+
+    def run(self, name, fn, *a, **kw):
+        t = self.torch
+        s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        s.record()
+        out = fn(*a, **kw)
+        e.record()
+        self.pending.append((name, s, e))
+        return out
+
+    def collect(self):
+        for name, s, e in self.pending:
+            self.total[name] = self.total.get(name, 0.0) + s.elapsed_time(e)
+            self.count[name] = self.count.get(name, 0) + 1
+        self.pending.clear()
+
+    def avg_ms(self, name):
+        return self.total[name] / self.count[name]
+
+
+def _traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    f = ROOT / "profiles" / "traffic.json"
+    if not f.exists():
+        return None
+    try:
+        data = json.loads(f.read_text())
+        ent = data["kernels"][kernel]
+        src = ROOT / ent["source"]
+        if hashlib.sha256(src.read_bytes()).hexdigest() != ent["source_sha256"]:
+            return None
+        return ent["fetch_bytes"] + ent["write_bytes"]
+    except (KeyError, ValueError, OSError):
+        return None
+
+
+def _flush_buffer(torch):
+    return torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards over heads with no "
+              "exchange, so per-GPU throughput is the N=1 figure. Nothing was run.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import attention_fa2_fwd_02_amd as fa2
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fa2.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+
+    w3, w5 = workloads.C3, workloads.C5
+    x = workloads.attn_inputs(w3, device=dev, with_do=True)
+    q, k, v, do = x["q"], x["k"], x["v"], x["do"]
+    o = torch.empty_like(q)
+    lse = torch.empty((w3.bh, w3.n_q), dtype=torch.float32, device=dev)
+    delta = torch.empty_like(lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    sc = w3.scale
+
+    timer = KernelTimer(torch)
+
+    def step():
+        timer.run("fwd", fa2.fa2_fwd, q, k, v, sc, o, lse)
+        timer.run("delta", fa2.fa2_bwd_delta, o, do, delta)
+        timer.run("dkdv", fa2.fa2_bwd_dkdv, q, k, v, do, lse, delta, sc, dk, dv)
+        timer.run("dq", fa2.fa2_bwd_dq, q, k, v, do, lse, delta, sc, dq)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timer.pending.clear()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    timer.collect()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    fwd_fl = w3.fwd_flops()
+    step_fl = fwd_fl + w3.bwd_flops()
+    value = step_fl / (ms_step * 1e-3) / 1e12
+
+    # per-kernel algorithmic work per launch
+    nqnkd = w3.bh * w3.n_q * w3.n_k * w3.head_dim
+    kern_flops = {"fwd": 4.0 * nqnkd, "dkdv": 8.0 * nqnkd, "dq": 6.0 * nqnkd}
+    es = 2
+    kern_bytes = {"delta": 2 * w3.bh * w3.n_q * w3.head_dim * es + w3.bh * w3.n_q * 4}
+    kernels = {}
+    for name in ("fwd", "delta", "dkdv", "dq"):
+        ms = timer.avg_ms(name)
+        ent = {"avg_ms": round(ms, 4)}
+        if name in kern_flops:
+            tf = kern_flops[name] / (ms * 1e-3) / 1e12
+            ent.update({"tflops": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+        else:
+            gbs = kern_bytes[name] / (ms * 1e-3) / 1e9
+            ent.update({"gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)})
+        kernels[name] = ent
+    dom = max(("fwd", "dkdv", "dq", "delta"), key=lambda n: timer.avg_ms(n))
+    dom_ms = timer.avg_ms(dom)
+    if dom in kern_flops:
+        ach = kern_flops[dom] / (dom_ms * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": _traffic(dom)}
+    else:
+        ach = kern_bytes[dom] / (dom_ms * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": _traffic(dom)}
+    print(f"[bench] main step {ms_step:.3f} ms, {value:.1f} TFLOP/s; kernels {kernels}", file=sys.stderr, flush=True)
+
+    legs = {}
+    if not args.no_legs:
+        del x, q, k, v, do, o, lse, delta, dq, dk, dv
+        torch.cuda.empty_cache()
+        legs = _legs(torch, fa2, workloads, dev)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = _cpu_baseline(w3, args.cpu_heads)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: i.i.d. N(0,1) bf16 Q, K, V, dO drawn on the device from seeded generators",
+        "config": {"workload": "llm_fwd_bwd: fa2_fwd + fa2_bwd_delta + fa2_bwd_dkdv + fa2_bwd_dq",
+                   "bh": w3.bh, "n_q": w3.n_q, "n_k": w3.n_k, "head_dim": w3.head_dim,
+                   "scale": w3.scale, "causal": False, "parallelism": "single GPU"},
+        "frac_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "wall_s_timed": round(wall, 3),
+        "kernels": kernels,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "legs": legs,
+        "device": {"name": props.name, "cus": props.multi_processor_count, "gcn_arch": getattr(props, "gcnArchName", "")},
+    }
+    print(json.dumps(out))
+
+
+def _time_fn(torch, fn, reps, warm=3, flush=None):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        if flush is not None:
+            flush.fill_(1)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        torch.cuda.synchronize()
+        ts.append(s.elapsed_time(e))
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
+def _legs(torch, fa2, workloads, dev):
+    legs = {}
+    # forward alone at the LLM shape
+    w3 = workloads.C3
+    x = workloads.attn_inputs(w3, device=dev)
+    o = torch.empty_like(x["q"])
+    lse = torch.empty((w3.bh, w3.n_q), dtype=torch.float32, device=dev)
+    ms = _time_fn(torch, lambda: fa2.fa2_fwd(x["q"], x["k"], x["v"], w3.scale, o, lse), 10)
+    tf = w3.fwd_flops() / (ms * 1e-3) / 1e12
+    legs["c3_fwd"] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    del x, o, lse
+    torch.cuda.empty_cache()
+    print(f"[bench] leg c3_fwd {legs['c3_fwd']}", file=sys.stderr, flush=True)
+
+    w4 = workloads.C4
+    x = workloads.attn_inputs(w4, device=dev)
+    o = torch.empty_like(x["q"])
+    lse = torch.empty((w4.bh, w4.n_q), dtype=torch.float32, device=dev)
+    ms = _time_fn(torch, lambda: fa2.fa2_fwd(x["q"], x["k"], x["v"], w4.scale, o, lse), 10)
+    tf = w4.fwd_flops() / (ms * 1e-3) / 1e12
+    legs["c4_xattn_fwd"] = {"ms": round(ms, 4), "tflops": round(tf, 1),
+                            "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    del x, o, lse
+    torch.cuda.empty_cache()
+    print(f"[bench] leg c4 {legs['c4_xattn_fwd']}", file=sys.stderr, flush=True)
+
+    w5 = workloads.C5
+    x = workloads.attn_inputs(w5, device=dev)
+    o, lse = fa2.fa2_fwd(x["q"], x["k"], x["v"], w5.scale)
+    delta = torch.empty_like(lse)
+    dq, dk, dv = (torch.empty_like(x["q"]) for _ in range(3))
+
+    def bwd():
+        fa2.fa2_bwd_delta(o, x["do"], delta)
+        fa2.fa2_bwd_dkdv(x["q"], x["k"], x["v"], x["do"], lse, delta, w5.scale, dk, dv)
+        fa2.fa2_bwd_dq(x["q"], x["k"], x["v"], x["do"], lse, delta, w5.scale, dq)
+
+    ms = _time_fn(torch, bwd, 10)
+    tf = w5.bwd_flops() / (ms * 1e-3) / 1e12
+    legs["c5_bwd"] = {"ms": round(ms, 4), "tflops_counted": round(tf, 1),
+                      "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    del x, o, lse, delta, dq, dk, dv
+    torch.cuda.empty_cache()
+    print(f"[bench] leg c5 {legs['c5_bwd']}", file=sys.stderr, flush=True)
+
+    w2 = workloads.C2
+    qkv = workloads.psa_inputs(w2, device=dev)
+    ws = {}
+    fa2.psa_block(qkv, w2.num_heads, w2.key_dim, ws)
+    byts = w2.algorithmic_bytes()
+    total_bytes = byts["pack"] + 2 * byts["attn_each"] + byts["merge"]
+    warm = _time_fn(torch, lambda: fa2.psa_block(qkv, w2.num_heads, w2.key_dim, ws), 50)
+    flush = _flush_buffer(torch)
+    cold = _time_fn(torch, lambda: fa2.psa_block(qkv, w2.num_heads, w2.key_dim, ws), 20, flush=flush)
+    del flush
+    legs["c2_psa_block"] = {
+        "us_per_call_warm": round(warm * 1e3, 2), "us_per_call_cold": round(cold * 1e3, 2),
+        "bytes": total_bytes,
+        "gbs_warm": round(total_bytes / (warm * 1e-3) / 1e9, 1),
+        "gbs_cold": round(total_bytes / (cold * 1e-3) / 1e9, 1),
+        "frac_hbm_cold": round(total_bytes / (cold * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "attn_tflops_warm": round(w2.attn_flops() / (warm * 1e-3) / 1e12, 2),
+    }
+    print(f"[bench] leg c2 {legs['c2_psa_block']}", file=sys.stderr, flush=True)
+    return legs
+
+
+def _cpu_baseline(w, heads_arg):
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads
+
+    threads = oracle.default_threads()
+    heads = heads_arg or threads
+    x = workloads.attn_inputs(w, device="cpu", bh=heads, with_do=True, seed=w.seed)
+    print(f"[bench] cpu baseline: oracle fwd+bwd on {heads} heads, {threads} threads", file=sys.stderr, flush=True)
+    q, k, v, do = (oracle._f64(x[n]) for n in ("q", "k", "v", "do"))
+    t0 = time.perf_counter()
+    oracle.attention_fwd(q, k, v, w.scale, threads)
+    oracle.attention_bwd(q, k, v, do, w.scale, threads)
+    secs = time.perf_counter() - t0
+    fl = 3.5 * 4.0 * heads * w.n_q * w.n_k * w.head_dim
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(fl / secs / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 oracle forward + backward of {heads} of the {w.bh} heads at full length "
+                      f"(n_q = n_k = {w.n_q}, head_dim {w.head_dim}), bf16-rounded inputs upcast to fp64; "
+                      f"{secs:.1f} s",
+            "seconds": round(secs, 2), "cpu_model": cpu_model, "host": platform.node()}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,143 @@
+/*
+ * fa2mi - exact FlashAttention-2 style attention for AMD Instinct MI355X
+ * (gfx950), plus the PSA pack/merge rearrangements around it.
+ *
+ * C ABI. Every pointer argument is a DEVICE pointer owned by the caller; the
+ * library never allocates, frees or keeps device memory and holds no state
+ * between calls. Every call only validates its arguments and enqueues one
+ * kernel on `stream` (a hipStream_t; NULL means the default stream), then
+ * returns: results are ready once the caller synchronises that stream.
+ *
+ * Layout (vision-rs flash_attn2.rs, module doc): attention tensors are flat
+ * [BH, N, HEAD_DIM] row-major and contiguous, BH = batch * heads; the caller
+ * reshapes [B, H, N, D] tensors to that layout. Query-side tensors (q, o, d_o,
+ * dq) are [bh, n_q, head_dim]; key-side tensors (k, v, dk, dv) are
+ * [bh, n_k, head_dim]; lse and delta are [bh, n_q] float32. Query and key
+ * lengths may differ (same page, "Forward": separate query and key lengths).
+ *
+ * Element types: all non-float32 tensors of one call share `dt`; accumulation
+ * is always float32; outputs are rounded to `dt` with round-to-nearest-even.
+ * lse and delta are always float32. LSE is in natural-log units.
+ *
+ * Supported: head_dim in {32, 64, 128}; non-causal attention without mask,
+ * dropout or bias (the pages describe none).
+ *
+ * Errors (checked on the host before anything is enqueued; nothing is enqueued
+ * when a call fails):
+ *   FA2_ERR_INVALID_ARG  a NULL pointer, a pointer not 16-byte aligned, a size
+ *                        <= 0, sizes whose per-head element count exceeds
+ *                        2^31 - 1, or an unknown dtype;
+ *   FA2_ERR_UNSUPPORTED  a head_dim / key_dim outside {32, 64, 128};
+ *   FA2_ERR_LAUNCH       the HIP runtime refused the launch.
+ * fa2_last_error() returns a message for the calling thread's last failure.
+ * Faults inside a kernel surface at the caller's next synchronisation.
+ * Outputs must not alias inputs. Calls on one stream run in order; calls on
+ * different streams writing the same buffers race.
+ */
+#ifndef FA2MI_H
+#define FA2MI_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA2_OK = 0,
+    FA2_ERR_INVALID_ARG = 1,
+    FA2_ERR_UNSUPPORTED = 2,
+    FA2_ERR_LAUNCH = 3
+} fa2_status;
+
+typedef enum { FA2_F32 = 0, FA2_F16 = 1, FA2_BF16 = 2 } fa2_dtype;
+
+/* Version of this ABI (bumped on any signature change). */
+int32_t fa2_abi_version(void);
+
+/* Short fixed description of a status code. */
+const char *fa2_status_str(fa2_status s);
+
+/* Detail message of the calling thread's most recent failed call ("" if none). */
+const char *fa2_last_error(void);
+
+/*
+ * Forward (vision-rs flash_attn2.rs, "Forward"; vyre-libs
+ * flash_attention_2.rs, the tiled builder): for every head b and query row i,
+ *   O[b,i,:]  = sum_j softmax_j(scale * q_i . k_j) v_j
+ *   lse[b,i]  = log(sum_j exp(scale * q_i . k_j))      (natural log)
+ * computed with the online-softmax recurrence over key tiles, so the
+ * n_q x n_k score matrix never reaches memory.
+ * In: q [bh,n_q,head_dim], k and v [bh,n_k,head_dim] (dt). Out: o
+ * [bh,n_q,head_dim] (dt), lse [bh,n_q] (float32), both fully overwritten.
+ * `scale` is the softmax scale (usually 1/sqrt(head_dim)).
+ */
+fa2_status fa2_fwd(fa2_dtype dt, const void *q, const void *k, const void *v, void *o, float *lse,
+                   int64_t bh, int64_t n_q, int64_t n_k, int32_t head_dim, float scale,
+                   void *stream);
+
+/*
+ * Backward pre-pass (vision-rs flash_attn2.rs, "Backward - dQ": the per-row
+ * term rowsum(O * dO)): delta[b,i] = sum_d o[b,i,d] * d_o[b,i,d] in float32.
+ * In: o, d_o [bh,n_q,head_dim] (dt). Out: delta [bh,n_q] float32, fully
+ * overwritten. Must run before fa2_bwd_dq / fa2_bwd_dkdv, which read delta.
+ */
+fa2_status fa2_bwd_delta(fa2_dtype dt, const void *o, const void *d_o, float *delta,
+                         int64_t bh, int64_t n_q, int32_t head_dim, void *stream);
+
+/*
+ * Backward, query side (vision-rs flash_attn2.rs, "Backward - dQ"): with
+ * p_ij = exp(scale * q_i . k_j - lse_i) recomputed from the saved lse,
+ *   dS_ij = p_ij * (d_o_i . v_j - delta_i),   dq_i = scale * sum_j dS_ij k_j.
+ * In: q, d_o [bh,n_q,head_dim]; k, v [bh,n_k,head_dim] (dt); lse, delta
+ * [bh,n_q] float32 from fa2_fwd and fa2_bwd_delta. Out: dq [bh,n_q,head_dim]
+ * (dt), fully overwritten (no zero-initialisation needed).
+ */
+fa2_status fa2_bwd_dq(fa2_dtype dt, const void *q, const void *k, const void *v, const void *d_o,
+                      const float *lse, const float *delta, void *dq,
+                      int64_t bh, int64_t n_q, int64_t n_k, int32_t head_dim, float scale,
+                      void *stream);
+
+/*
+ * Backward, key side (vision-rs flash_attn2.rs, "Backward - dK / dV"): with
+ * p_ij and dS_ij as above,
+ *   dv_j = sum_i p_ij d_o_i,   dk_j = scale * sum_i dS_ij q_i.
+ * Inputs as for fa2_bwd_dq. Out: dk, dv [bh,n_k,head_dim] (dt), fully
+ * overwritten. Deterministic: no atomics.
+ */
+fa2_status fa2_bwd_dkdv(fa2_dtype dt, const void *q, const void *k, const void *v, const void *d_o,
+                        const float *lse, const float *delta, void *dk, void *dv,
+                        int64_t bh, int64_t n_q, int64_t n_k, int32_t head_dim, float scale,
+                        void *stream);
+
+/*
+ * PSA pack (vision_rs psa.rs, "psa_pack_qkv"): qkv is the NCHW output of the
+ * block's qkv convolution, [batch, num_heads*4*key_dim, h, w]; per head its
+ * channels are Q, K, V_lo, V_hi, key_dim each. Writes
+ *   packed[s][b*num_heads + hd][n][d] = qkv[b][hd*4*key_dim + s*key_dim + d][n]
+ * for sections s = 0 Q, 1 K, 2 V_lo, 3 V_hi and pixel n < h*w: packed is
+ * [4, batch*num_heads, h*w, key_dim], so each section is a ready [BH, N, D]
+ * operand for fa2_fwd (Q, K, V_lo or V_hi). Bit-exact copy. dt is F16, BF16
+ * or F32; key_dim in {32, 64, 128}.
+ */
+fa2_status psa_pack_qkv(fa2_dtype dt, const void *qkv, void *packed,
+                        int32_t batch, int32_t num_heads, int32_t key_dim, int32_t h, int32_t w,
+                        void *stream);
+
+/*
+ * PSA merge (vision_rs psa.rs, "psa_merge_attn_nchw"): o_lo and o_hi are the
+ * attention outputs for V_lo and V_hi, [batch*num_heads, h*w, key_dim];
+ * writes out NCHW [batch, num_heads*2*key_dim, h, w] with
+ *   out[b][hd*2*key_dim + d][n]           = o_lo[b*num_heads + hd][n][d]
+ *   out[b][hd*2*key_dim + key_dim + d][n] = o_hi[b*num_heads + hd][n][d].
+ * Bit-exact copy.
+ */
+fa2_status psa_merge_attn(fa2_dtype dt, const void *o_lo, const void *o_hi, void *out,
+                          int32_t batch, int32_t num_heads, int32_t key_dim, int32_t h, int32_t w,
+                          void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA2MI_H */

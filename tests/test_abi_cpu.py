@@ -1,0 +1,95 @@
+"""CPU checks of the C-ABI boundary: the built library loads, exports every
+function include/fa2mi.h declares, and rejects invalid arguments with the
+documented status codes before anything is enqueued (these calls never reach
+the HIP runtime, so they run without a GPU). The Python binding refuses CPU
+tensors instead of computing anything on the host."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import attention_fa2_fwd_02_amd as fa2
+from attention_fa2_fwd_02_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa2mi.h")
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+A = 0x10000        # a 16-byte aligned fake device address (never dereferenced)
+MIS = 0x10008      # misaligned
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:fa2|psa)_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = fa2.load()
+    names = _declared()
+    assert set(names) == set(_lib.SIGNATURES), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    lib = fa2.load()
+    assert lib.fa2_abi_version() == 1
+    assert lib.fa2_status_str(0) == b"ok"
+    assert lib.fa2_status_str(2) == b"unsupported size"
+
+
+def _fwd(**kw):
+    a = dict(dt=2, q=A, k=A, v=A, o=A, lse=A, bh=2, n_q=64, n_k=64, d=64, scale=0.125, stream=None)
+    a.update(kw)
+    lib = fa2.load()
+    return lib.fa2_fwd(a["dt"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["bh"], a["n_q"], a["n_k"], a["d"],
+                       a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"q": None}, INVALID), ({"lse": None}, INVALID), ({"v": MIS}, INVALID),
+    ({"bh": 0}, INVALID), ({"n_q": 0}, INVALID), ({"n_k": -3}, INVALID), ({"dt": 7}, INVALID),
+    ({"d": 48}, UNSUPPORTED), ({"d": 256}, UNSUPPORTED), ({"d": 0}, INVALID),
+    ({"scale": float("nan")}, INVALID), ({"scale": float("inf")}, INVALID),
+    ({"n_q": 1 << 25, "d": 128}, INVALID),          # n*d over 2^31-1 per head
+    ({"bh": 1 << 40, "n_q": 1 << 20}, INVALID),     # grid over 2^31-1 workgroups
+])
+def test_fwd_rejects_invalid_arguments(kw, code):
+    assert _fwd(**kw) == code
+    assert fa2.load().fa2_last_error().startswith(b"fa2_fwd: ")
+
+
+def test_bwd_and_psa_reject_invalid_arguments():
+    lib = fa2.load()
+    assert lib.fa2_bwd_delta(2, A, None, A, 2, 64, 64, None) == INVALID
+    assert lib.fa2_bwd_delta(2, A, A, A, 2, 64, 96, None) == UNSUPPORTED
+    assert lib.fa2_bwd_dq(2, A, A, A, A, A, None, A, 2, 64, 64, 64, 0.1, None) == INVALID
+    assert lib.fa2_bwd_dq(2, A, A, A, A, A, A, A, 2, 64, 64, 16, 0.1, None) == UNSUPPORTED
+    assert lib.fa2_bwd_dkdv(2, A, A, A, A, A, A, A, MIS, 2, 64, 64, 64, 0.1, None) == INVALID
+    assert lib.fa2_bwd_dkdv(1, A, A, A, A, A, A, A, A, 2, 64, 0, 64, 0.1, None) == INVALID
+    assert lib.psa_pack_qkv(1, A, None, 16, 4, 32, 20, 20, None) == INVALID
+    assert lib.psa_pack_qkv(1, A, A, 16, 4, 40, 20, 20, None) == UNSUPPORTED
+    assert lib.psa_pack_qkv(1, A, A, 16, 0, 32, 20, 20, None) == INVALID
+    assert lib.psa_merge_attn(1, A, A, MIS, 16, 4, 32, 20, 20, None) == INVALID
+    assert lib.psa_merge_attn(5, A, A, A, 16, 4, 32, 20, 20, None) == INVALID
+    assert b"psa_merge_attn" in lib.fa2_last_error()
+
+
+def test_binding_refuses_host_tensors():
+    q = torch.zeros(1, 8, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa2.fa2_fwd(q, q, q)
+    x = torch.zeros(1, 4 * 32, 2, 2, dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa2.psa_pack_qkv(x, 1, 32)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_LIB_PATH", tmp_path / "libfa2mi.so")
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.load()
