@@ -38,8 +38,8 @@ fa2_status check_attn(const char *fn, fa2_dtype dt, int64_t bh, int64_t n_q, int
     if (!good_dim(head_dim)) return fail(FA2_ERR_UNSUPPORTED, fn, "head_dim must be 32, 64 or 128");
     if (n_q * head_dim > INT_MAX || n_k * head_dim > INT_MAX)
         return fail(FA2_ERR_INVALID_ARG, fn, "n * head_dim exceeds 2^31 - 1 elements per head");
-    if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
-        return fail(FA2_ERR_INVALID_ARG, fn, "scale must be finite");
+    if (!(scale > 0.f) || scale == __builtin_inff())
+        return fail(FA2_ERR_INVALID_ARG, fn, "scale must be positive and finite");
     const int64_t blocks = (grid_rows + rows_per_block - 1) / rows_per_block;
     if (bh > INT_MAX / blocks) return fail(FA2_ERR_INVALID_ARG, fn, "grid exceeds 2^31 - 1 workgroups");
     return FA2_OK;

@@ -365,7 +365,6 @@ static hipError_t dq_dispatch(const void *q, const void *k, const void *v, const
                               const float *delta, void *dq, const AttnShape &s, hipStream_t stream) {
     using elem = typename Traits<DT>::elem;
     constexpr int WAVES = 4, BC = 64, BR = 32 * WAVES;
-    static_assert(BR == kFwdRowsPerBlock, "row block");
     const int nqb = (s.n_q + BR - 1) / BR;
     const int total = (int)(s.bh * nqb);
     const float scale_log2 = (float)((double)s.scale * 1.4426950408889634);

@@ -32,6 +32,9 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// Largest log2 gap allowed between a score and the reference max before the
+// forward rescales (keeps probabilities <= 2^8 = 256).
+constexpr float kRescaleLog2 = 8.f;
 
 enum class Dt { F32 = 0, F16 = 1, BF16 = 2 };
 
@@ -130,24 +133,25 @@ __device__ __forceinline__ typename Traits<DT>::frag c_to_frag(const f32x16 &c, 
 
 // ---------------------------------------------------------------------------
 // Cooperative tile staging: an R x D row-major global tile is moved by the
-// workgroup in 4-row x VEC-column blocks (VEC = one 16-byte vector), each
+// workgroup in RB-row x VEC-column blocks (VEC = one 16-byte vector), each
 // thread owning whole blocks. Rows at or beyond `valid` are zero-filled.
 // COL_FAST numbers blocks along a row first (neighbouring lanes read
 // neighbouring 16-byte pieces of one row: best for tiles kept row-major in
 // LDS); otherwise down a column first (neighbouring lanes write neighbouring
-// 4-row runs of one transposed LDS row: conflict-free transposed stores).
+// RB-row runs of one transposed LDS row: conflict-free transposed stores).
 
-template <Dt DT, int R, int D, int NT, bool COL_FAST = true>
+template <Dt DT, int R, int D, int NT, bool COL_FAST = true, int RB = 4>
 struct TileStage {
     using elem = typename Traits<DT>::elem;
     static constexpr int VEC = vec_elems<DT>();
-    static constexpr int BLOCKS = (R / 4) * (D / VEC);
+    static constexpr int BLOCKS = (R / RB) * (D / VEC);
     static constexpr int PER_THREAD = (BLOCKS + NT - 1) / NT;
-    static_assert(R % 4 == 0 && D % VEC == 0, "tile shape");
-    uint4 v[PER_THREAD][4];
+    static_assert(R % RB == 0 && D % VEC == 0, "tile shape");
+    static_assert(RB == 1 || RB == 2 || RB == 4, "block height");
+    uint4 v[PER_THREAD][RB];
 
-    __device__ static constexpr int row_block(int blk) { return COL_FAST ? blk / (D / VEC) : blk % (R / 4); }
-    __device__ static constexpr int col_block(int blk) { return COL_FAST ? blk % (D / VEC) : blk / (R / 4); }
+    __device__ static constexpr int row_block(int blk) { return COL_FAST ? blk / (D / VEC) : blk % (R / RB); }
+    __device__ static constexpr int col_block(int blk) { return COL_FAST ? blk % (D / VEC) : blk / (R / RB); }
 
     // Global -> registers. `base` points at row 0 of the tile; row stride D.
     __device__ __forceinline__ void load(const elem *__restrict__ base, int valid, int tid) {
@@ -156,9 +160,9 @@ struct TileStage {
             const int blk = tid + i * NT;
             const int rb = row_block(blk), cb = col_block(blk);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = rb * 4 + r;
-                if (blk < BLOCKS && row < valid)
+            for (int r = 0; r < RB; ++r) {
+                const int row = rb * RB + r;
+                if ((BLOCKS % NT == 0 || blk < BLOCKS) && row < valid)
                     v[i][r] = *reinterpret_cast<const uint4 *>(base + (int64_t)row * D + cb * VEC);
                 else
                     v[i][r] = make_uint4(0, 0, 0, 0);
@@ -172,54 +176,72 @@ struct TileStage {
 #pragma unroll
         for (int i = 0; i < PER_THREAD; ++i) {
             const int blk = tid + i * NT;
-            if (blk >= BLOCKS) break;
+            if (BLOCKS % NT != 0 && blk >= BLOCKS) break;
             const int rb = row_block(blk), cb = col_block(blk);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                *reinterpret_cast<uint4 *>(lds + (rb * 4 + r) * LD + cb * VEC) = v[i][r];
+            for (int r = 0; r < RB; ++r)
+                *reinterpret_cast<uint4 *>(lds + (rb * RB + r) * LD + cb * VEC) = v[i][r];
         }
     }
 
     // Registers -> LDS transposed: element (row, col) goes to lds[col*LD + row],
-    // so each 4-row block column becomes one 4-element run.
+    // so each RB-row block column becomes one RB-element run.
     template <int LD>
     __device__ __forceinline__ void store_transposed(elem *lds, int tid) const {
 #pragma unroll
         for (int i = 0; i < PER_THREAD; ++i) {
             const int blk = tid + i * NT;
-            if (blk >= BLOCKS) break;
+            if (BLOCKS % NT != 0 && blk >= BLOCKS) break;
             const int rb = row_block(blk), cb = col_block(blk);
+            const uint32_t *w[RB];
+#pragma unroll
+            for (int r = 0; r < RB; ++r) w[r] = reinterpret_cast<const uint32_t *>(&v[i][r]);
             if constexpr (sizeof(elem) == 2) {
-                const uint32_t *r0 = reinterpret_cast<const uint32_t *>(&v[i][0]);
-                const uint32_t *r1 = reinterpret_cast<const uint32_t *>(&v[i][1]);
-                const uint32_t *r2 = reinterpret_cast<const uint32_t *>(&v[i][2]);
-                const uint32_t *r3 = reinterpret_cast<const uint32_t *>(&v[i][3]);
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
                     // columns 2p (low halves) and 2p+1 (high halves)
-                    uint2 even, odd;
-                    even.x = (r0[p] & 0xffffu) | (r1[p] << 16);
-                    even.y = (r2[p] & 0xffffu) | (r3[p] << 16);
-                    odd.x = (r0[p] >> 16) | (r1[p] & 0xffff0000u);
-                    odd.y = (r2[p] >> 16) | (r3[p] & 0xffff0000u);
                     const int col = cb * VEC + 2 * p;
-                    *reinterpret_cast<uint2 *>(lds + col * LD + rb * 4) = even;
-                    *reinterpret_cast<uint2 *>(lds + (col + 1) * LD + rb * 4) = odd;
+                    elem *e0 = lds + col * LD + rb * RB;
+                    elem *e1 = lds + (col + 1) * LD + rb * RB;
+                    if constexpr (RB == 4) {
+                        uint2 even, odd;
+                        even.x = (w[0][p] & 0xffffu) | (w[1][p] << 16);
+                        even.y = (w[2][p] & 0xffffu) | (w[3][p] << 16);
+                        odd.x = (w[0][p] >> 16) | (w[1][p] & 0xffff0000u);
+                        odd.y = (w[2][p] >> 16) | (w[3][p] & 0xffff0000u);
+                        *reinterpret_cast<uint2 *>(e0) = even;
+                        *reinterpret_cast<uint2 *>(e1) = odd;
+                    } else if constexpr (RB == 2) {
+                        *reinterpret_cast<uint32_t *>(e0) = (w[0][p] & 0xffffu) | (w[1][p] << 16);
+                        *reinterpret_cast<uint32_t *>(e1) = (w[0][p] >> 16) | (w[1][p] & 0xffff0000u);
+                    } else {
+                        *reinterpret_cast<uint16_t *>(e0) = (uint16_t)(w[0][p] & 0xffffu);
+                        *reinterpret_cast<uint16_t *>(e1) = (uint16_t)(w[0][p] >> 16);
+                    }
                 }
             } else {
-                const uint32_t *r0 = reinterpret_cast<const uint32_t *>(&v[i][0]);
-                const uint32_t *r1 = reinterpret_cast<const uint32_t *>(&v[i][1]);
-                const uint32_t *r2 = reinterpret_cast<const uint32_t *>(&v[i][2]);
-                const uint32_t *r3 = reinterpret_cast<const uint32_t *>(&v[i][3]);
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
-                    const int col = cb * VEC + p;
-                    *reinterpret_cast<uint4 *>(lds + col * LD + rb * 4) = make_uint4(r0[p], r1[p], r2[p], r3[p]);
+                    elem *e = lds + (cb * VEC + p) * LD + rb * RB;
+                    if constexpr (RB == 4)
+                        *reinterpret_cast<uint4 *>(e) = make_uint4(w[0][p], w[1][p], w[2][p], w[3][p]);
+                    else if constexpr (RB == 2)
+                        *reinterpret_cast<uint2 *>(e) = make_uint2(w[0][p], w[1][p]);
+                    else
+                        *reinterpret_cast<uint32_t *>(e) = w[0][p];
                 }
             }
         }
     }
 };
+
+// Block height that gives each of NT threads one staging block of an R x D
+// tile when possible (4 rows at most).
+template <Dt DT, int R, int D, int NT>
+constexpr int stage_rows() {
+    constexpr int r = (R * (D / vec_elems<DT>())) / NT;
+    return r >= 4 ? 4 : (r >= 2 ? 2 : 1);
+}
 
 // Maps the hardware workgroup id to a logical tile id so that the tiles one
 // XCD runs are contiguous in logical order (same heads -> shared K/V in that
@@ -232,7 +254,16 @@ __device__ __forceinline__ int xcd_remap(int hw_id, int total) {
 }
 
 // Max / sum with the lane 32 apart (the other half of a C block column).
-__device__ __forceinline__ float xhalf_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
-__device__ __forceinline__ float xhalf_sum(float x) { return x + __shfl_xor(x, 32); }
+// v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second; with x in both, the two results hold, in every
+// lane, x of that lane and x of the lane 32 apart (in some order).
+__device__ __forceinline__ float xhalf_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 }  // namespace fa2mi

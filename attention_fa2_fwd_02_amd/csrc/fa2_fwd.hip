@@ -9,10 +9,12 @@
 //      tile is fetched into registers while the current one is computed.
 //   2. S^T = K Q^T on MFMA: one C block per 32 keys; each lane owns one query
 //      (the C column), so a row's max needs one exchange between lane halves.
-//   3. Online softmax in the log2 domain (scale*log2(e) folded into one
-//      multiply, exp2): m' = max(m, rowmax), alpha = 2^(m - m'), P = 2^(S - m'),
-//      l = alpha*l + rowsum(P) (lane-partial sums, combined at the end).
-//   4. O^T = alpha*O^T + V^T P^T on MFMA, P fed from registers as the B operand.
+//   3. Online softmax in the log2 domain (scale*log2(e) folded into one FMA
+//      before exp2): P = 2^(S - m), l += rowsum(P) (lane-partial sums,
+//      combined at the end). The reference max m is raised lazily: only when
+//      a row max exceeds it by more than kRescaleLog2, and then O and l are
+//      rescaled by 2^(m - m') as in the online-softmax recurrence.
+//   4. O^T += V^T P^T on MFMA, P fed from registers as the B operand.
 // Epilogue: O = O^T / l rounded to the element type; LSE = ln2 * (m + log2 l).
 #include "fa2_device.h"
 #include "fa2_launch.h"
@@ -48,7 +50,7 @@ __device__ __forceinline__ void store4(typename Traits<DT>::elem *dst, const f32
 }
 
 template <Dt DT, int D, int BC, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void fwd_kernel(
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(
     const typename Traits<DT>::elem *__restrict__ Q, const typename Traits<DT>::elem *__restrict__ K,
     const typename Traits<DT>::elem *__restrict__ V, typename Traits<DT>::elem *__restrict__ O,
     float *__restrict__ LSE, int n_q, int n_k, int n_qblocks, int total_blocks, float scale_log2) {
@@ -92,16 +94,20 @@ __global__ __launch_bounds__(WAVES * 64) void fwd_kernel(
     f32x16 acc[NDB];
 #pragma unroll
     for (int i = 0; i < NDB; ++i) acc[i] = zero16();
-    float m_run = -INFINITY, l_run = 0.f;
+    // m_ref: the reference max (log2 units) the probabilities of this row are
+    // taken against; l_run: lane-partial sum of those probabilities.
+    float m_ref = -INFINITY, l_run = 0.f;
 
-    TileStage<DT, BC, D, NT, true> kst;
-    TileStage<DT, BC, D, NT, false> vst;
+    constexpr int RBS = stage_rows<DT, BC, D, NT>();
+    TileStage<DT, BC, D, NT, true, RBS> kst;
+    TileStage<DT, BC, D, NT, false, RBS> vst;
     const int ntiles = (n_k + BC - 1) / BC;
     kst.load(K + koff, n_k, tid);
     vst.load(V + koff, n_k, tid);
     kst.template store_rows<LDK>(Ks, tid);
     vst.template store_transposed<LDV>(Vt, tid);
     __syncthreads();
+
 
     for (int it = 0; it < ntiles; ++it) {
         const int j0 = it * BC;
@@ -110,8 +116,11 @@ __global__ __launch_bounds__(WAVES * 64) void fwd_kernel(
             kst.load(K + koff + (int64_t)(j0 + BC) * D, n_k - j0 - BC, tid);
             vst.load(V + koff + (int64_t)(j0 + BC) * D, n_k - j0 - BC, tid);
         }
-
-        // S^T = K Q^T, one 32x32 block per 32 keys
+        // mask: the tile is the ragged last one (keys >= kvalid do not exist
+        // and get probability 0)
+        const int kvalid = n_k - j0;
+        const bool mask = kvalid < BC;
+        // S^T = K Q^T (raw dot products), one 32x32 block per 32 keys
         f32x16 s[NKB];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
@@ -120,39 +129,46 @@ __global__ __launch_bounds__(WAVES * 64) void fwd_kernel(
 #pragma unroll
             for (int t = 0; t < TS; ++t) s[kb] = Tr::mfma(ld_row_frag<DT>(krow, t, h), qf[t], s[kb]);
         }
-
-        // online softmax, log2 domain
-        const int kvalid = n_k - j0;
+        // lane-partial max of the raw scores (scale > 0, so the max commutes
+        // with scaling)
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int c = 0; c < 16; ++c) {
-                float x = s[kb][c] * scale_log2;
-                if (kvalid < BC && 32 * kb + crow(c, h) >= kvalid) x = -INFINITY;
-                s[kb][c] = x;
-                mx = fmaxf(mx, x);
+                if (mask) {
+                    if (32 * kb + crow(c, h) >= kvalid) s[kb][c] = -INFINITY;
+                }
+                mx = fmaxf(mx, s[kb][c]);
             }
-        mx = xhalf_max(mx);
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        // Lazy rescaling: the reference max only moves when some row's max
+        // exceeds it by more than kRescaleLog2 (probabilities then stay
+        // <= 2^kRescaleLog2). Moving it rescales O and l by 2^(m_ref - m_new),
+        // the online-softmax correction; the final O = acc / l is unchanged.
+        const float mx2 = mx * scale_log2;
+        if (__any(mx2 > m_ref + kRescaleLog2)) {
+            const float m_new = fmaxf(m_ref, xhalf_max(mx2));
+            const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int c = 0; c < 16; ++c) acc[db][c] *= alpha;
+            l_run *= alpha;
+            m_ref = m_new;
+        }
         float rs = 0.f;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int c = 0; c < 16; ++c) {
-                const float p = __builtin_amdgcn_exp2f(s[kb][c] - m_new);
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][c], scale_log2, -m_ref));
                 s[kb][c] = p;
                 rs += p;
             }
-        l_run = l_run * alpha + rs;
-        m_run = m_new;
-
-        // O^T = alpha O^T + V^T P^T
+        l_run += rs;
+        // O^T += V^T P^T
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-            for (int c = 0; c < 16; ++c) acc[db][c] *= alpha;
             const elem *vrow = Vt + (32 * db + col) * LDV;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
@@ -177,24 +193,33 @@ __global__ __launch_bounds__(WAVES * 64) void fwd_kernel(
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) store4<DT>(op + 32 * db + 8 * g + 4 * h, acc[db], g, inv);
-        if (h == 0) LSE[(int64_t)bh * n_q + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+        if (h == 0) LSE[(int64_t)bh * n_q + qrow] = (m_ref + __log2f(l_tot)) * kLn2;
     }
 }
 
-template <Dt DT, int D>
-static hipError_t fwd_dispatch(const void *q, const void *k, const void *v, void *o, float *lse,
-                               const AttnShape &s, hipStream_t stream) {
+template <Dt DT, int D, int WAVES>
+static hipError_t fwd_launch(const void *q, const void *k, const void *v, void *o, float *lse, const AttnShape &s,
+                             hipStream_t stream) {
     using elem = typename Traits<DT>::elem;
-    constexpr int WAVES = 4, BC = 64;
-    constexpr int BR = 32 * WAVES;
-    static_assert(BR == kFwdRowsPerBlock, "row block");
+    constexpr int BC = 64, BR = 32 * WAVES;
     const int nqb = (s.n_q + BR - 1) / BR;
     const int total = (int)(s.bh * nqb);
     const float scale_log2 = (float)((double)s.scale * 1.4426950408889634);
-    hipLaunchKernelGGL((fwd_kernel<DT, D, BC, WAVES>), dim3(total), dim3(WAVES * 64), 0, stream,
-                       (const elem *)q, (const elem *)k, (const elem *)v, (elem *)o, lse, s.n_q, s.n_k,
-                       nqb, total, scale_log2);
+    hipLaunchKernelGGL((fwd_kernel<DT, D, BC, WAVES>), dim3(total), dim3(WAVES * 64), 0, stream, (const elem *)q,
+                       (const elem *)k, (const elem *)v, (elem *)o, lse, s.n_q, s.n_k, nqb, total, scale_log2);
     return hipGetLastError();
+}
+
+// Workgroup size by problem size: 8 waves (256 query rows, K/V tiles shared by
+// the most rows) when that still gives every CU at least two workgroups,
+// else 4 or 2 waves so that small problems still spread over the chip.
+template <Dt DT, int D>
+static hipError_t fwd_dispatch(const void *q, const void *k, const void *v, void *o, float *lse,
+                               const AttnShape &s, hipStream_t stream) {
+    constexpr int64_t kCus = 256;
+    if (s.bh * ((s.n_q + 255) / 256) >= 2 * kCus) return fwd_launch<DT, D, 8>(q, k, v, o, lse, s, stream);
+    if (s.bh * ((s.n_q + 127) / 128) >= kCus) return fwd_launch<DT, D, 4>(q, k, v, o, lse, s, stream);
+    return fwd_launch<DT, D, 2>(q, k, v, o, lse, s, stream);
 }
 
 template <Dt DT>

@@ -38,9 +38,9 @@ hipError_t launch_psa_pack(int dt, const void *qkv, void *packed, const PsaShape
 hipError_t launch_psa_merge(int dt, const void *lo, const void *hi, void *out, const PsaShape &s,
                             hipStream_t stream);
 
-// Query rows per forward / dq workgroup and key rows per dkdv workgroup
-// (the ABI checks that the 1-D grids fit in int32).
-constexpr int kFwdRowsPerBlock = 128;
+// Smallest query rows per forward / dq workgroup and key rows per dkdv
+// workgroup (the ABI checks that the 1-D grids fit in int32).
+constexpr int kFwdRowsPerBlock = 64;
 constexpr int kDkdvKeysPerBlock = 128;
 
 }  // namespace fa2mi

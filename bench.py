@@ -46,6 +46,9 @@ def _parse():
     ap.add_argument("--no-legs", action="store_true", help="skip the other-shape legs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0, help="oracle sample heads (0: one per thread)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed steps, run a plain 1 GiB device copy three times (reference kernel "
+                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
 
 
@@ -181,6 +184,14 @@ def main():
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": _traffic(dom)}
     print(f"[bench] main step {ms_step:.3f} ms, {value:.1f} TFLOP/s; kernels {kernels}", file=sys.stderr, flush=True)
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(3)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     legs = {}
     if not args.no_legs:

@@ -26,7 +26,8 @@
  * when a call fails):
  *   FA2_ERR_INVALID_ARG  a NULL pointer, a pointer not 16-byte aligned, a size
  *                        <= 0, sizes whose per-head element count exceeds
- *                        2^31 - 1, or an unknown dtype;
+ *                        2^31 - 1, a softmax scale that is not positive and
+ *                        finite, or an unknown dtype;
  *   FA2_ERR_UNSUPPORTED  a head_dim / key_dim outside {32, 64, 128};
  *   FA2_ERR_LAUNCH       the HIP runtime refused the launch.
  * fa2_last_error() returns a message for the calling thread's last failure.
@@ -70,7 +71,7 @@ const char *fa2_last_error(void);
  * n_q x n_k score matrix never reaches memory.
  * In: q [bh,n_q,head_dim], k and v [bh,n_k,head_dim] (dt). Out: o
  * [bh,n_q,head_dim] (dt), lse [bh,n_q] (float32), both fully overwritten.
- * `scale` is the softmax scale (usually 1/sqrt(head_dim)).
+ * `scale` is the softmax scale (usually 1/sqrt(head_dim)); it must be > 0.
  */
 fa2_status fa2_fwd(fa2_dtype dt, const void *q, const void *k, const void *v, void *o, float *lse,
                    int64_t bh, int64_t n_q, int64_t n_k, int32_t head_dim, float scale,

@@ -55,6 +55,7 @@ def _fwd(**kw):
     ({"bh": 0}, INVALID), ({"n_q": 0}, INVALID), ({"n_k": -3}, INVALID), ({"dt": 7}, INVALID),
     ({"d": 48}, UNSUPPORTED), ({"d": 256}, UNSUPPORTED), ({"d": 0}, INVALID),
     ({"scale": float("nan")}, INVALID), ({"scale": float("inf")}, INVALID),
+    ({"scale": 0.0}, INVALID), ({"scale": -0.125}, INVALID),
     ({"n_q": 1 << 25, "d": 128}, INVALID),          # n*d over 2^31-1 per head
     ({"bh": 1 << 40, "n_q": 1 << 20}, INVALID),     # grid over 2^31-1 workgroups
 ])

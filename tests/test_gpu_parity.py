@@ -81,12 +81,18 @@ def test_fwd_c1_tiny_f32():
 
 
 def test_fwd_single_key_passes_values_through():
-    # one key: the softmax is [1], so O = V exactly (vyre-libs tests, seq_len 1)
+    # one key: the softmax is [1], so O = V (vyre-libs tests, seq_len 1). In
+    # float32 the kernel's P = 2^e with |e| an fp32 rounding error, so O = V up
+    # to a few fp32 ulps; bfloat16 output rounds that back to V exactly.
     for dt in ("f32", "bf16"):
         x = _inputs(dt, 3, 77, 1, 64, seed=5)
         o, lse = fa2.fa2_fwd(x["q"], x["k"], x["v"])
         torch.cuda.synchronize()
-        assert torch.equal(o, x["v"].expand(-1, 77, -1)), dt
+        want = x["v"].expand(-1, 77, -1)
+        if dt == "bf16":
+            assert torch.equal(o, want), dt
+        else:
+            assert torch.allclose(o, want, rtol=1e-6, atol=0), dt
         want = (x["q"].double() @ x["k"].double().transpose(1, 2)).squeeze(-1) / 8.0
         assert torch.allclose(lse.double(), want, atol=1e-4), dt
 
