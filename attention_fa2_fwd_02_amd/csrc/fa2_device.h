@@ -235,6 +235,76 @@ struct TileStage {
     }
 };
 
+// ---------------------------------------------------------------------------
+// Buffer resources: a raw buffer over one head's rows. Loads at byte offsets
+// at or past `bytes` return zero (hardware range check), which zero-fills the
+// rows of a ragged last tile without branches.
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+// Row-major R x D tile staging through registers with buffer loads: thread
+// tid owns PER_THREAD 16-byte pieces, numbered along rows first.
+template <Dt DT, int R, int D, int NT>
+struct RowStage {
+    using elem = typename Traits<DT>::elem;
+    static constexpr int VEC = vec_elems<DT>();
+    static constexpr int PIECES = R * (D / VEC);
+    static constexpr int PER_THREAD = (PIECES + NT - 1) / NT;
+    uint4 v[PER_THREAD];
+
+    // rows row0 .. row0+R-1 of the buffer (row stride D elements)
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, int row0, int tid) {
+#pragma unroll
+        for (int i = 0; i < PER_THREAD; ++i) {
+            const int pc = tid + i * NT;
+            const int row = pc / (D / VEC), cv = pc % (D / VEC);
+            if (PIECES % NT == 0 || pc < PIECES)
+                v[i] = buffer_load16(rsrc, (uint32_t)(((row0 + row) * D + cv * VEC) * (int)sizeof(elem)));
+        }
+    }
+
+    template <int LD>
+    __device__ __forceinline__ void store(elem *lds, int tid) const {
+#pragma unroll
+        for (int i = 0; i < PER_THREAD; ++i) {
+            const int pc = tid + i * NT;
+            const int row = pc / (D / VEC), cv = pc % (D / VEC);
+            if (PIECES % NT == 0 || pc < PIECES)
+                *reinterpret_cast<uint4 *>(lds + row * LD + cv * VEC) = v[i];
+        }
+    }
+};
+
+// A fragment (32 rows d x 16 keys) of V^T read from a ROW-MAJOR V tile in LDS
+// (row = key, stride LD elements) with the gfx950 transposing LDS read
+// ds_read_b64_tr_b16. Within each 16-lane group that instruction returns to
+// lane j, as element r, element (j % 4) of the 4-element chunk addressed by
+// lane 4r + j/4 of the group. Lane l of group g therefore points at
+//   V[key0 + 4H + l/4][d0 + 16(g%2) + 4(l%4)]   (H = g/2 = lane half)
+// so that lane j receives V[key0 + 4H + r][d0 + 16(g%2) + j], r = 0..3: the
+// keys of C-block registers fed back as a B operand (see crow). Two reads
+// cover the slots of keys +0..3 and +8..11 of the 16-key step.
+template <Dt DT>
+__device__ __forceinline__ typename Traits<DT>::frag ld_vt_frag_tr(const typename Traits<DT>::elem *vtile, int LD,
+                                                                   int key0, int d0, int lane) {
+    static_assert(Traits<DT>::KPL == 8, "16-bit element types only");
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    const int l = lane & 15, g = lane >> 4, hh = g >> 1;
+    const typename Traits<DT>::elem *p = vtile + (key0 + 4 * hh + (l >> 2)) * LD + d0 + 16 * (g & 1) + 4 * (l & 3);
+    using lds_i16x4 = __attribute__((address_space(3))) i16x4;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 8 * LD));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(typename Traits<DT>::frag, both);
+}
+
 // Block height that gives each of NT threads one staging block of an R x D
 // tile when possible (4 rows at most).
 template <Dt DT, int R, int D, int NT>

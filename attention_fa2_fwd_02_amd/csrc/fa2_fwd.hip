@@ -16,6 +16,8 @@
 //      rescaled by 2^(m - m') as in the online-softmax recurrence.
 //   4. O^T += V^T P^T on MFMA, P fed from registers as the B operand.
 // Epilogue: O = O^T / l rounded to the element type; LSE = ln2 * (m + log2 l).
+#include <type_traits>
+
 #include "fa2_device.h"
 #include "fa2_launch.h"
 
@@ -49,6 +51,98 @@ __device__ __forceinline__ void store4(typename Traits<DT>::elem *dst, const f32
     }
 }
 
+// One key tile of the forward for one wave: scores, online softmax with lazy
+// rescaling, and the P V accumulation. MASK: the tile is the ragged last one
+// and keys at or beyond kvalid do not exist (probability 0).
+template <Dt DT, int D, int BC, bool MASK>
+__device__ __forceinline__ void fwd_tile(const typename Traits<DT>::elem *kt, const typename Traits<DT>::elem *vt,
+                                         const typename Traits<DT>::frag (&qf)[D / (2 * Traits<DT>::KPL)],
+                                         f32x16 (&acc)[D / 32], float &m_ref, float &l_run, float scale_log2,
+                                         int kvalid, int lane) {
+    using Tr = Traits<DT>;
+    using elem = typename Tr::elem;
+    using frag = typename Tr::frag;
+    constexpr bool TR = sizeof(elem) == 2;
+    constexpr int KPL = Tr::KPL;
+    constexpr int KSTEP = 2 * KPL;
+    constexpr int VEC = vec_elems<DT>();
+    constexpr int LDK = D + VEC;
+    constexpr int LDV = TR ? D + 2 * VEC : BC + 4;
+    constexpr int NKB = BC / 32;
+    constexpr int NDB = D / 32;
+    constexpr int TS = D / KSTEP;
+    constexpr int TP = 32 / KSTEP;
+    const int h = lane >> 5, col = lane & 31;
+    // S^T = K Q^T (raw dot products), one 32x32 block per 32 keys; the
+    // two blocks' accumulation chains are interleaved.
+    f32x16 s[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = zero16();
+#pragma unroll
+    for (int t = 0; t < TS; ++t)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+            s[kb] = Tr::mfma(ld_row_frag<DT>(kt + (32 * kb + col) * LDK, t, h), qf[t], s[kb]);
+
+    // ragged last tile: keys >= kvalid do not exist (probability 0)
+    if constexpr (MASK) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int c = 0; c < 16; ++c)
+                if (32 * kb + crow(c, h) >= kvalid) s[kb][c] = -INFINITY;
+    }
+    // lane-partial max of the raw scores (scale > 0, so the max commutes
+    // with scaling)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int c = 0; c < 16; ++c) mx = fmaxf(mx, s[kb][c]);
+    // Lazy rescaling: the reference max only moves when some row's max
+    // exceeds it by more than kRescaleLog2 (probabilities then stay
+    // <= 2^kRescaleLog2). Moving it rescales O and l by 2^(m_ref - m_new),
+    // the online-softmax correction; the final O = acc / l is unchanged.
+    const float mx2 = mx * scale_log2;
+    if (__any(mx2 > m_ref + kRescaleLog2)) {
+        __asm__ volatile("" ::: "memory");
+        const float m_new = fmaxf(m_ref, xhalf_max(mx2));
+        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int c = 0; c < 16; ++c) acc[db][c] *= alpha;
+        l_run *= alpha;
+        m_ref = m_new;
+    }
+    const float neg_m = -m_ref;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][c], scale_log2, neg_m));
+            s[kb][c] = p;
+            l_run += p;
+        }
+    // O^T += V^T P^T: per 16-key step, one P fragment feeds all d blocks
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int t = 0; t < TP; ++t) {
+            const frag pf = c_to_frag<DT>(s[kb], t);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                frag vf;
+                if constexpr (TR)
+                    vf = ld_vt_frag_tr<DT>(vt, LDV, 32 * kb + 16 * t, 32 * db, lane);
+                else
+                    vf = ld_t_frag<DT>(vt + (32 * db + col) * LDV, kb, t, h);
+                acc[db] = Tr::mfma(vf, pf, acc[db]);
+            }
+        }
+
+}
+
 template <Dt DT, int D, int BC, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(
     const typename Traits<DT>::elem *__restrict__ Q, const typename Traits<DT>::elem *__restrict__ K,
@@ -57,21 +151,25 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     using Tr = Traits<DT>;
     using elem = typename Tr::elem;
     using frag = typename Tr::frag;
+    constexpr bool TR = sizeof(elem) == 2;  // V read with ds_read_b64_tr_b16
     constexpr int NT = WAVES * 64;
     constexpr int BR = 32 * WAVES;
     constexpr int KPL = Tr::KPL;
     constexpr int KSTEP = 2 * KPL;
     constexpr int VEC = vec_elems<DT>();
-    constexpr int LDK = D + VEC;  // row-major K tile stride (16-byte pad)
-    constexpr int LDV = BC + 4;   // transposed V tile stride
-    constexpr int NKB = BC / 32;  // 32-key blocks per tile
-    constexpr int NDB = D / 32;   // 32-row blocks of O^T
-    constexpr int TS = D / KSTEP; // contraction steps over head_dim
-    constexpr int TP = 32 / KSTEP;// contraction steps per 32-key block
+    constexpr int LDK = D + VEC;            // K tile: row-major, 16-byte pad
+    constexpr int LDV = TR ? D + 2 * VEC    // V tile: row-major, 32-byte pad
+                           : BC + 4;        //   (f32: transposed, keys contiguous)
+    constexpr int KS = BC * LDK;            // elements per K stage
+    constexpr int VS = TR ? BC * LDV : D * LDV;
+    constexpr int NKB = BC / 32;            // 32-key blocks per tile
+    constexpr int NDB = D / 32;             // 32-row blocks of O^T
+    constexpr int TS = D / KSTEP;           // contraction steps over head_dim
+    constexpr int TP = 32 / KSTEP;          // contraction steps per 32-key block
     static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
 
-    __shared__ __attribute__((aligned(16))) elem Ks[BC * LDK];
-    __shared__ __attribute__((aligned(16))) elem Vt[D * LDV];
+    __shared__ __attribute__((aligned(16))) elem Ks[2 * KS];
+    __shared__ __attribute__((aligned(16))) elem Vs[2 * VS];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, col = lane & 31;
@@ -98,92 +196,60 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     // taken against; l_run: lane-partial sum of those probabilities.
     float m_ref = -INFINITY, l_run = 0.f;
 
+    // K/V tiles: buffer loads over this head's rows (rows past n_k read as
+    // zero) into registers, then into one of two LDS stages.
+    const uint32_t head_bytes = (uint32_t)n_k * D * (uint32_t)sizeof(elem);
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + koff, head_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + koff, head_bytes);
+    RowStage<DT, BC, D, NT> kst;
     constexpr int RBS = stage_rows<DT, BC, D, NT>();
-    TileStage<DT, BC, D, NT, true, RBS> kst;
-    TileStage<DT, BC, D, NT, false, RBS> vst;
+    using VStage = std::conditional_t<TR, RowStage<DT, BC, D, NT>, TileStage<DT, BC, D, NT, false, RBS>>;
+    VStage vst;
+    auto vload = [&](int row0) {
+        if constexpr (TR)
+            vst.load(vrs, row0, tid);
+        else
+            vst.load(V + koff + (int64_t)row0 * D, n_k - row0, tid);
+    };
+    auto vstore = [&](elem *dst) {
+        if constexpr (TR)
+            vst.template store<LDV>(dst, tid);
+        else
+            vst.template store_transposed<LDV>(dst, tid);
+    };
+
     const int ntiles = (n_k + BC - 1) / BC;
-    kst.load(K + koff, n_k, tid);
-    vst.load(V + koff, n_k, tid);
-    kst.template store_rows<LDK>(Ks, tid);
-    vst.template store_transposed<LDV>(Vt, tid);
+    const int nfull = n_k / BC;  // full tiles; a ragged last one follows when n_k % BC != 0
+    kst.load(krs, 0, tid);
+    vload(0);
+    kst.template store<LDK>(Ks, tid);
+    vstore(Vs);
+    if (ntiles > 1) {
+        kst.load(krs, BC, tid);
+        vload(BC);
+    }
     __syncthreads();
 
-
-    for (int it = 0; it < ntiles; ++it) {
+    for (int it = 0; it < nfull; ++it) {
         const int j0 = it * BC;
-        const bool more = it + 1 < ntiles;
-        if (more) {
-            kst.load(K + koff + (int64_t)(j0 + BC) * D, n_k - j0 - BC, tid);
-            vst.load(V + koff + (int64_t)(j0 + BC) * D, n_k - j0 - BC, tid);
-        }
-        // mask: the tile is the ragged last one (keys >= kvalid do not exist
-        // and get probability 0)
-        const int kvalid = n_k - j0;
-        const bool mask = kvalid < BC;
-        // S^T = K Q^T (raw dot products), one 32x32 block per 32 keys
-        f32x16 s[NKB];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            s[kb] = zero16();
-            const elem *krow = Ks + (32 * kb + col) * LDK;
-#pragma unroll
-            for (int t = 0; t < TS; ++t) s[kb] = Tr::mfma(ld_row_frag<DT>(krow, t, h), qf[t], s[kb]);
-        }
-        // lane-partial max of the raw scores (scale > 0, so the max commutes
-        // with scaling)
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                if (mask) {
-                    if (32 * kb + crow(c, h) >= kvalid) s[kb][c] = -INFINITY;
-                }
-                mx = fmaxf(mx, s[kb][c]);
+        fwd_tile<DT, D, BC, false>(Ks + (it & 1) * KS, Vs + (it & 1) * VS, qf, acc, m_ref, l_run, scale_log2, BC,
+                                   lane);
+        // next tile (already in registers) into the other stage; then fetch
+        // the one after. One barrier per tile: it orders this tile's reads of
+        // a stage before that stage is refilled two tiles later.
+        if (it + 1 < ntiles) {
+            kst.template store<LDK>(Ks + ((it + 1) & 1) * KS, tid);
+            vstore(Vs + ((it + 1) & 1) * VS);
+            if (it + 2 < ntiles) {
+                kst.load(krs, j0 + 2 * BC, tid);
+                vload(j0 + 2 * BC);
             }
-        // Lazy rescaling: the reference max only moves when some row's max
-        // exceeds it by more than kRescaleLog2 (probabilities then stay
-        // <= 2^kRescaleLog2). Moving it rescales O and l by 2^(m_ref - m_new),
-        // the online-softmax correction; the final O = acc / l is unchanged.
-        const float mx2 = mx * scale_log2;
-        if (__any(mx2 > m_ref + kRescaleLog2)) {
-            const float m_new = fmaxf(m_ref, xhalf_max(mx2));
-            const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int c = 0; c < 16; ++c) acc[db][c] *= alpha;
-            l_run *= alpha;
-            m_ref = m_new;
-        }
-        float rs = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][c], scale_log2, -m_ref));
-                s[kb][c] = p;
-                rs += p;
-            }
-        l_run += rs;
-        // O^T += V^T P^T
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-            const elem *vrow = Vt + (32 * db + col) * LDV;
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int t = 0; t < TP; ++t)
-                    acc[db] = Tr::mfma(ld_t_frag<DT>(vrow, kb, t, h), c_to_frag<DT>(s[kb], t), acc[db]);
-        }
-
-        __syncthreads();
-        if (more) {
-            kst.template store_rows<LDK>(Ks, tid);
-            vst.template store_transposed<LDV>(Vt, tid);
         }
         __syncthreads();
     }
+    if (nfull < ntiles)
+        fwd_tile<DT, D, BC, true>(Ks + (nfull & 1) * KS, Vs + (nfull & 1) * VS, qf, acc, m_ref, l_run, scale_log2,
+                                  n_k - nfull * BC, lane);
 
     const float l_tot = xhalf_sum(l_run);
     if (qrow < n_q) {
