@@ -69,11 +69,37 @@ __global__ __launch_bounds__(256) void delta_kernel(const typename Traits<DT>::e
 }
 
 // ---------------------------------------------------------------------------
-// dQ: per workgroup BR = 32*WAVES query rows; key tiles of BC rows staged as
-// K row-major (for S^T = K Q^T), K transposed (for dQ^T = K^T dS^T) and V
-// row-major (for dP^T = V dO^T). Each lane owns one query column.
+// Shared pieces of the two gradient kernels. Tiles come in through raw
+// buffer loads over one head's rows (rows past the end read as zero) and sit
+// row-major in LDS in two stages; transposed MFMA operands are read from the
+// row-major tiles with ds_read_b64_tr_b16 (16-bit types) or, for float32,
+// from a transposed copy. No masking is needed: a key past n_k has zero K
+// and V rows and so adds nothing to dQ; a query past n_q has zero Q and dO
+// rows and so adds nothing to dK or dV.
+
+// A fragment of T^T (32 columns d of a row-major tile T x 16 of its rows, in
+// the row order of C-block registers fed back as B operands), rows key0 ..
+template <Dt DT, int LD, int LDT>
+__device__ __forceinline__ typename Traits<DT>::frag ld_trans_frag(const typename Traits<DT>::elem *rowtile,
+                                                                   const typename Traits<DT>::elem *ttile,
+                                                                   int kb, int t, int db, int lane) {
+    if constexpr (sizeof(typename Traits<DT>::elem) == 2) {
+        (void)ttile;
+        return ld_vt_frag_tr<DT>(rowtile, LD, 32 * kb + 16 * t, 32 * db, lane);
+    } else {
+        (void)rowtile;
+        return ld_t_frag<DT>(ttile + (32 * db + (lane & 31)) * LDT, kb, t, lane >> 5);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: per workgroup BR = 32*WAVES query rows (one 32-row block per wave, each
+// lane owning one query column), looping over key tiles of BC rows:
+//   S^T = K Q^T, dP^T = V dO^T (K, V row-major A operands from LDS; Q, dO
+//   B operands from registers), P = 2^(S*scale*log2e - lse*log2e),
+//   dS = P (dP - delta), dQ^T += K^T dS^T (K^T via transposing reads).
 template <Dt DT, int D, int BC, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void dq_kernel(
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(
     const typename Traits<DT>::elem *__restrict__ Q, const typename Traits<DT>::elem *__restrict__ K,
     const typename Traits<DT>::elem *__restrict__ V, const typename Traits<DT>::elem *__restrict__ dO,
     const float *__restrict__ LSE, const float *__restrict__ Delta, typename Traits<DT>::elem *__restrict__ dQ,
@@ -81,21 +107,24 @@ __global__ __launch_bounds__(WAVES * 64) void dq_kernel(
     using Tr = Traits<DT>;
     using elem = typename Tr::elem;
     using frag = typename Tr::frag;
+    constexpr bool TR = sizeof(elem) == 2;
     constexpr int NT = WAVES * 64;
     constexpr int BR = 32 * WAVES;
     constexpr int KPL = Tr::KPL;
     constexpr int KSTEP = 2 * KPL;
     constexpr int VEC = vec_elems<DT>();
     constexpr int LDK = D + VEC;
-    constexpr int LDT = BC + 4;
+    constexpr int LDT = BC + 4;          // float32 transposed K copy
+    constexpr int KS = BC * LDK;
+    constexpr int TSZ = TR ? 1 : D * LDT;
     constexpr int NKB = BC / 32;
     constexpr int NDB = D / 32;
     constexpr int TS = D / KSTEP;
     constexpr int TP = 32 / KSTEP;
 
-    __shared__ __attribute__((aligned(16))) elem Ks[BC * LDK];
-    __shared__ __attribute__((aligned(16))) elem Vs[BC * LDK];
-    __shared__ __attribute__((aligned(16))) elem Kt[D * LDT];
+    __shared__ __attribute__((aligned(16))) elem Ks[2 * KS];
+    __shared__ __attribute__((aligned(16))) elem Vs[2 * KS];
+    __shared__ __attribute__((aligned(16))) elem Kt[2 * TSZ];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, col = lane & 31;
@@ -107,7 +136,8 @@ __global__ __launch_bounds__(WAVES * 64) void dq_kernel(
     const bool qvalid = qrow < n_q;
 
     frag qf[TS], df[TS];
-    float lse2 = 0.f, dl = 0.f;
+    // invalid rows: zero operands and lse = +inf, so every P is 0
+    float lse2 = INFINITY, dl = 0.f;
     if (qvalid) {
         const elem *qp = Q + qoff + (int64_t)qrow * D;
         const elem *dp = dO + qoff + (int64_t)qrow * D;
@@ -127,29 +157,39 @@ __global__ __launch_bounds__(WAVES * 64) void dq_kernel(
 #pragma unroll
     for (int i = 0; i < NDB; ++i) acc[i] = zero16();
 
-    TileStage<DT, BC, D, NT, true> kst, vst;
+    const uint32_t head_bytes = (uint32_t)n_k * D * (uint32_t)sizeof(elem);
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + koff, head_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + koff, head_bytes);
+    RowStage<DT, BC, D, NT> kst, vst;
+    constexpr int RBS = stage_rows<DT, BC, D, NT>();
+    TileStage<DT, BC, D, NT, false, RBS> ktst;  // float32 only: transposed K
+    auto load = [&](int row0) {
+        kst.load(krs, row0, tid);
+        vst.load(vrs, row0, tid);
+        if constexpr (!TR) ktst.load(K + koff + (int64_t)row0 * D, n_k - row0, tid);
+    };
+    auto store = [&](int stage) {
+        kst.template store<LDK>(Ks + stage * KS, tid);
+        vst.template store<LDK>(Vs + stage * KS, tid);
+        if constexpr (!TR) ktst.template store_transposed<LDT>(Kt + stage * TSZ, tid);
+    };
+
     const int ntiles = (n_k + BC - 1) / BC;
-    kst.load(K + koff, n_k, tid);
-    vst.load(V + koff, n_k, tid);
-    kst.template store_rows<LDK>(Ks, tid);
-    kst.template store_transposed<LDT>(Kt, tid);
-    vst.template store_rows<LDK>(Vs, tid);
+    load(0);
+    store(0);
+    if (ntiles > 1) load(BC);
     __syncthreads();
 
     for (int it = 0; it < ntiles; ++it) {
-        const int j0 = it * BC;
-        const bool more = it + 1 < ntiles;
-        if (more) {
-            kst.load(K + koff + (int64_t)(j0 + BC) * D, n_k - j0 - BC, tid);
-            vst.load(V + koff + (int64_t)(j0 + BC) * D, n_k - j0 - BC, tid);
-        }
-        const int kvalid = n_k - j0;
-        f32x16 ds[NKB];
+        const int st = it & 1;
+        const elem *kt = Ks + st * KS;
+        const elem *vt = Vs + st * KS;
+        const elem *ktt = Kt + st * TSZ;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             f32x16 s = zero16(), dp = zero16();
-            const elem *krow = Ks + (32 * kb + col) * LDK;
-            const elem *vrow = Vs + (32 * kb + col) * LDK;
+            const elem *krow = kt + (32 * kb + col) * LDK;
+            const elem *vrow = vt + (32 * kb + col) * LDK;
 #pragma unroll
             for (int t = 0; t < TS; ++t) {
                 s = Tr::mfma(ld_row_frag<DT>(krow, t, h), qf[t], s);
@@ -157,26 +197,20 @@ __global__ __launch_bounds__(WAVES * 64) void dq_kernel(
             }
 #pragma unroll
             for (int c = 0; c < 16; ++c) {
-                float x = s[c] * scale_log2 - lse2;
-                if (kvalid < BC && 32 * kb + crow(c, h) >= kvalid) x = -INFINITY;
-                const float p = qvalid ? __builtin_amdgcn_exp2f(x) : 0.f;
-                ds[kb][c] = p * (dp[c] - dl);
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c], scale_log2, -lse2));
+                s[c] = p * (dp[c] - dl);
+            }
+#pragma unroll
+            for (int t = 0; t < TP; ++t) {
+                const frag dsf = c_to_frag<DT>(s, t);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    acc[db] = Tr::mfma(ld_trans_frag<DT, LDK, LDT>(kt, ktt, kb, t, db, lane), dsf, acc[db]);
             }
         }
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-            const elem *trow = Kt + (32 * db + col) * LDT;
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int t = 0; t < TP; ++t)
-                    acc[db] = Tr::mfma(ld_t_frag<DT>(trow, kb, t, h), c_to_frag<DT>(ds[kb], t), acc[db]);
-        }
-        __syncthreads();
-        if (more) {
-            kst.template store_rows<LDK>(Ks, tid);
-            kst.template store_transposed<LDT>(Kt, tid);
-            vst.template store_rows<LDK>(Vs, tid);
+        if (it + 1 < ntiles) {
+            store((it + 1) & 1);
+            if (it + 2 < ntiles) load((it + 2) * BC);
         }
         __syncthreads();
     }
@@ -193,9 +227,10 @@ __global__ __launch_bounds__(WAVES * 64) void dq_kernel(
 // ---------------------------------------------------------------------------
 // dK, dV: per workgroup BKV = 32*WAVES key rows, wave w owning keys
 // 32w..32w+31 with their K and V rows in registers (B operands). Query tiles
-// of BQ rows are staged as Q and dO row-major (A operands of S = Q K^T and
-// dP = dO V^T) and transposed (A operands of dK^T = Q^T dS, dV^T = dO^T P),
-// plus log2-scaled LSE and delta. C blocks: rows = queries, column = key.
+// of BQ rows: Q and dO row-major in LDS (A operands of S = Q K^T and
+// dP = dO V^T, and via transposing reads of dK^T += Q^T dS and
+// dV^T += dO^T P), plus lse*log2e and delta. C blocks: rows = queries,
+// column = key; lse and delta vary along a lane's registers.
 template <Dt DT, int D, int BQ, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void dkdv_kernel(
     const typename Traits<DT>::elem *__restrict__ Q, const typename Traits<DT>::elem *__restrict__ K,
@@ -206,6 +241,7 @@ __global__ __launch_bounds__(WAVES * 64) void dkdv_kernel(
     using Tr = Traits<DT>;
     using elem = typename Tr::elem;
     using frag = typename Tr::frag;
+    constexpr bool TR = sizeof(elem) == 2;
     constexpr int NT = WAVES * 64;
     constexpr int BKV = 32 * WAVES;
     constexpr int KPL = Tr::KPL;
@@ -213,18 +249,20 @@ __global__ __launch_bounds__(WAVES * 64) void dkdv_kernel(
     constexpr int VEC = vec_elems<DT>();
     constexpr int LDQ = D + VEC;
     constexpr int LDT = BQ + 4;
+    constexpr int QS = BQ * LDQ;
+    constexpr int TSZ = TR ? 1 : D * LDT;
     constexpr int NQB = BQ / 32;
     constexpr int NDB = D / 32;
     constexpr int TS = D / KSTEP;
     constexpr int TP = 32 / KSTEP;
     static_assert(BQ <= NT, "lse staging");
 
-    __shared__ __attribute__((aligned(16))) elem Qs[BQ * LDQ];
-    __shared__ __attribute__((aligned(16))) elem Ds[BQ * LDQ];
-    __shared__ __attribute__((aligned(16))) elem Qt[D * LDT];
-    __shared__ __attribute__((aligned(16))) elem Dt_[D * LDT];
-    __shared__ __attribute__((aligned(16))) float Ls[BQ];
-    __shared__ __attribute__((aligned(16))) float Dl[BQ];
+    __shared__ __attribute__((aligned(16))) elem Qs[2 * QS];
+    __shared__ __attribute__((aligned(16))) elem Ds[2 * QS];
+    __shared__ __attribute__((aligned(16))) elem Qt[2 * TSZ];
+    __shared__ __attribute__((aligned(16))) elem Dt_[2 * TSZ];
+    __shared__ __attribute__((aligned(16))) float Ls[2 * BQ];
+    __shared__ __attribute__((aligned(16))) float Dl[2 * BQ];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, col = lane & 31;
@@ -253,84 +291,95 @@ __global__ __launch_bounds__(WAVES * 64) void dkdv_kernel(
 #pragma unroll
     for (int i = 0; i < NDB; ++i) accK[i] = accV[i] = zero16();
 
-    TileStage<DT, BQ, D, NT, true> qst, dst;
+    const uint32_t head_bytes = (uint32_t)n_q * D * (uint32_t)sizeof(elem);
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + qoff, head_bytes);
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(dO + qoff, head_bytes);
+    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(LSE + loff, (uint32_t)n_q * 4u);
+    const __amdgpu_buffer_rsrc_t ers = make_rsrc(Delta + loff, (uint32_t)n_q * 4u);
+    RowStage<DT, BQ, D, NT> qst, dst;
+    constexpr int RBS = stage_rows<DT, BQ, D, NT>();
+    TileStage<DT, BQ, D, NT, false, RBS> qtst, dtst;  // float32 only: transposed copies
+    float lreg = 0.f, dreg = 0.f;
+    auto load = [&](int row0) {
+        qst.load(qrs, row0, tid);
+        dst.load(drs, row0, tid);
+        if (tid < BQ) {
+            // rows past n_q read as 0: their Q and dO rows are zero, so their
+            // terms vanish whatever P is
+            lreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrs, (row0 + tid) * 4, 0, 0));
+            dreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ers, (row0 + tid) * 4, 0, 0));
+        }
+        if constexpr (!TR) {
+            qtst.load(Q + qoff + (int64_t)row0 * D, n_q - row0, tid);
+            dtst.load(dO + qoff + (int64_t)row0 * D, n_q - row0, tid);
+        }
+    };
+    auto store = [&](int stage) {
+        qst.template store<LDQ>(Qs + stage * QS, tid);
+        dst.template store<LDQ>(Ds + stage * QS, tid);
+        if (tid < BQ) {
+            Ls[stage * BQ + tid] = lreg * kLog2e;
+            Dl[stage * BQ + tid] = dreg;
+        }
+        if constexpr (!TR) {
+            qtst.template store_transposed<LDT>(Qt + stage * TSZ, tid);
+            dtst.template store_transposed<LDT>(Dt_ + stage * TSZ, tid);
+        }
+    };
+
     const int ntiles = (n_q + BQ - 1) / BQ;
-    float lreg = INFINITY, dreg = 0.f;
-    qst.load(Q + qoff, n_q, tid);
-    dst.load(dO + qoff, n_q, tid);
-    if (tid < BQ && tid < n_q) {
-        lreg = LSE[loff + tid] * kLog2e;
-        dreg = Delta[loff + tid];
-    }
-    qst.template store_rows<LDQ>(Qs, tid);
-    qst.template store_transposed<LDT>(Qt, tid);
-    dst.template store_rows<LDQ>(Ds, tid);
-    dst.template store_transposed<LDT>(Dt_, tid);
-    if (tid < BQ) {
-        Ls[tid] = lreg;
-        Dl[tid] = dreg;
-    }
+    load(0);
+    store(0);
+    if (ntiles > 1) load(BQ);
     __syncthreads();
 
     for (int it = 0; it < ntiles; ++it) {
-        const int i0 = it * BQ;
-        const bool more = it + 1 < ntiles;
-        if (more) {
-            qst.load(Q + qoff + (int64_t)(i0 + BQ) * D, n_q - i0 - BQ, tid);
-            dst.load(dO + qoff + (int64_t)(i0 + BQ) * D, n_q - i0 - BQ, tid);
-            lreg = INFINITY;
-            dreg = 0.f;
-            if (tid < BQ && i0 + BQ + tid < n_q) {
-                lreg = LSE[loff + i0 + BQ + tid] * kLog2e;
-                dreg = Delta[loff + i0 + BQ + tid];
-            }
-        }
+        const int st = it & 1;
+        const elem *qt = Qs + st * QS;
+        const elem *dt = Ds + st * QS;
+        const elem *qtt = Qt + st * TSZ;
+        const elem *dtt = Dt_ + st * TSZ;
+        const float *ls = Ls + st * BQ;
+        const float *dls = Dl + st * BQ;
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
             f32x16 s = zero16(), dp = zero16();
-            const elem *qrow = Qs + (32 * qb + col) * LDQ;
-            const elem *drow = Ds + (32 * qb + col) * LDQ;
+            const elem *qrow = qt + (32 * qb + col) * LDQ;
+            const elem *drow = dt + (32 * qb + col) * LDQ;
 #pragma unroll
             for (int t = 0; t < TS; ++t) {
                 s = Tr::mfma(ld_row_frag<DT>(qrow, t, h), kf[t], s);
                 dp = Tr::mfma(ld_row_frag<DT>(drow, t, h), vf[t], dp);
             }
-            f32x16 p, ds;
+            // p into s, dS into dp
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const float4 l4 = *reinterpret_cast<const float4 *>(Ls + 32 * qb + 8 * g + 4 * h);
-                const float4 d4 = *reinterpret_cast<const float4 *>(Dl + 32 * qb + 8 * g + 4 * h);
+                const float4 l4 = *reinterpret_cast<const float4 *>(ls + 32 * qb + 8 * g + 4 * h);
+                const float4 d4 = *reinterpret_cast<const float4 *>(dls + 32 * qb + 8 * g + 4 * h);
                 const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
                 const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int c = 4 * g + i;
-                    const float pv = __builtin_amdgcn_exp2f(s[c] * scale_log2 - lv[i]);
-                    p[c] = pv;
-                    ds[c] = pv * (dp[c] - dv[i]);
+                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c], scale_log2, -lv[i]));
+                    s[c] = pv;
+                    dp[c] = pv * (dp[c] - dv[i]);
                 }
             }
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const elem *dtr = Dt_ + (32 * db + col) * LDT;
-                const elem *qtr = Qt + (32 * db + col) * LDT;
+            for (int t = 0; t < TP; ++t) {
+                const frag pf = c_to_frag<DT>(s, t);
+                const frag dsf = c_to_frag<DT>(dp, t);
 #pragma unroll
-                for (int t = 0; t < TP; ++t) {
-                    accV[db] = Tr::mfma(ld_t_frag<DT>(dtr, qb, t, h), c_to_frag<DT>(p, t), accV[db]);
-                    accK[db] = Tr::mfma(ld_t_frag<DT>(qtr, qb, t, h), c_to_frag<DT>(ds, t), accK[db]);
+                for (int db = 0; db < NDB; ++db) {
+                    accV[db] = Tr::mfma(ld_trans_frag<DT, LDQ, LDT>(dt, dtt, qb, t, db, lane), pf, accV[db]);
+                    accK[db] = Tr::mfma(ld_trans_frag<DT, LDQ, LDT>(qt, qtt, qb, t, db, lane), dsf, accK[db]);
                 }
             }
         }
-        __syncthreads();
-        if (more) {
-            qst.template store_rows<LDQ>(Qs, tid);
-            qst.template store_transposed<LDT>(Qt, tid);
-            dst.template store_rows<LDQ>(Ds, tid);
-            dst.template store_transposed<LDT>(Dt_, tid);
-            if (tid < BQ) {
-                Ls[tid] = lreg;
-                Dl[tid] = dreg;
-            }
+        if (it + 1 < ntiles) {
+            store((it + 1) & 1);
+            if (it + 2 < ntiles) load((it + 2) * BQ);
         }
         __syncthreads();
     }
@@ -360,11 +409,12 @@ static hipError_t delta_dispatch(const void *o, const void *d_o, float *delta, i
     return hipGetLastError();
 }
 
-template <Dt DT, int D>
-static hipError_t dq_dispatch(const void *q, const void *k, const void *v, const void *d_o, const float *lse,
-                              const float *delta, void *dq, const AttnShape &s, hipStream_t stream) {
+template <Dt DT, int D, int WAVES>
+static hipError_t dq_launch(const void *q, const void *k, const void *v, const void *d_o, const float *lse,
+                            const float *delta, void *dq, const AttnShape &s, hipStream_t stream) {
     using elem = typename Traits<DT>::elem;
-    constexpr int WAVES = 4, BC = 64, BR = 32 * WAVES;
+    // float32 at head_dim 128 halves the key tile to fit two LDS stages
+    constexpr int BC = (sizeof(elem) == 4 && D == 128) ? 32 : 64, BR = 32 * WAVES;
     const int nqb = (s.n_q + BR - 1) / BR;
     const int total = (int)(s.bh * nqb);
     const float scale_log2 = (float)((double)s.scale * 1.4426950408889634);
@@ -375,10 +425,20 @@ static hipError_t dq_dispatch(const void *q, const void *k, const void *v, const
 }
 
 template <Dt DT, int D>
+static hipError_t dq_dispatch(const void *q, const void *k, const void *v, const void *d_o, const float *lse,
+                              const float *delta, void *dq, const AttnShape &s, hipStream_t stream) {
+    constexpr int64_t kCus = 256;
+    if (s.bh * ((s.n_q + 255) / 256) >= 2 * kCus) return dq_launch<DT, D, 8>(q, k, v, d_o, lse, delta, dq, s, stream);
+    if (s.bh * ((s.n_q + 127) / 128) >= kCus) return dq_launch<DT, D, 4>(q, k, v, d_o, lse, delta, dq, s, stream);
+    return dq_launch<DT, D, 2>(q, k, v, d_o, lse, delta, dq, s, stream);
+}
+
+template <Dt DT, int D>
 static hipError_t dkdv_dispatch(const void *q, const void *k, const void *v, const void *d_o, const float *lse,
                                 const float *delta, void *dk, void *dv, const AttnShape &s, hipStream_t stream) {
     using elem = typename Traits<DT>::elem;
-    constexpr int WAVES = 4, BQ = 64, BKV = 32 * WAVES;
+    constexpr int WAVES = 4, BKV = 32 * WAVES;
+    constexpr int BQ = (sizeof(elem) == 4 && D == 128) ? 32 : 64;
     static_assert(BKV == kDkdvKeysPerBlock, "key block");
     const int nkb = (s.n_k + BKV - 1) / BKV;
     const int total = (int)(s.bh * nkb);
