@@ -77,20 +77,48 @@ __global__ __launch_bounds__(256) void delta_kernel(const typename Traits<DT>::e
 // and V rows and so adds nothing to dQ; a query past n_q has zero Q and dO
 // rows and so adds nothing to dK or dV.
 
-// A fragment of T^T (32 columns d of a row-major tile T x 16 of its rows, in
-// the row order of C-block registers fed back as B operands), rows key0 ..
-template <Dt DT, int LD, int LDT>
-__device__ __forceinline__ typename Traits<DT>::frag ld_trans_frag(const typename Traits<DT>::elem *rowtile,
-                                                                   const typename Traits<DT>::elem *ttile,
-                                                                   int kb, int t, int db, int lane) {
-    if constexpr (sizeof(typename Traits<DT>::elem) == 2) {
-        (void)ttile;
-        return ld_vt_frag_tr<DT>(rowtile, LD, 32 * kb + 16 * t, 32 * db, lane);
-    } else {
-        (void)rowtile;
-        return ld_t_frag<DT>(ttile + (32 * db + (lane & 31)) * LDT, kb, t, lane >> 5);
+// Tile access for the gradient kernels. 16-bit types: padded row-major tiles
+// read as rows (ds_read_b128) and, for transposed operands, with
+// ds_read_b64_tr_b16. The gfx950 LDS behaves as 64 four-byte banks;
+// ds_read_b128 serves 16 lanes per cycle (16 consecutive rows, one 16-byte
+// chunk each) and ds_read_b64_tr_b16 32 lanes per cycle (4 consecutive rows,
+// 64 bytes each). A row stride of an odd number of 16-byte chunks keeps the
+// first pattern conflict-free; with 19 chunks at D = 128 (9 at 64, 5 at 32)
+// the second is at most 2-way. (An XOR swizzle removes both conflicts but
+// costs more address arithmetic than the conflicts it saves.) float32:
+// padded row-major tiles plus a transposed copy (stride LDT).
+template <Dt DT, int D>
+struct BwdTile {
+    using elem = typename Traits<DT>::elem;
+    using frag = typename Traits<DT>::frag;
+    static constexpr bool TR = sizeof(elem) == 2;
+    static constexpr int VEC = vec_elems<DT>();
+    static constexpr int LD = TR ? (D == 128 ? D + 3 * VEC : D + VEC) : D + VEC;  // row stride
+
+    // row fragment (contraction step t over head_dim) of tile row `row`
+    __device__ static __forceinline__ frag row(const elem *tile, int row, int t, int h) {
+        return ld_row_frag<DT>(tile + row * LD, t, h);
     }
-}
+
+    // A fragment of T^T: columns 32db.. of the tile x its rows 32kb + 16t ..
+    // in the row order of C-block registers fed back as B operands
+    template <int LDT>
+    __device__ static __forceinline__ frag trans(const elem *tile, const elem *ttile, int kb, int t, int db,
+                                                 int lane) {
+        if constexpr (TR) {
+            (void)ttile;
+            return ld_vt_frag_tr<DT>(tile, LD, 32 * kb + 16 * t, 32 * db, lane);
+        } else {
+            (void)tile;
+            return ld_t_frag<DT>(ttile + (32 * db + (lane & 31)) * LDT, kb, t, lane >> 5);
+        }
+    }
+
+    template <int R, int NT>
+    __device__ static __forceinline__ void store(const RowStage<DT, R, D, NT> &st, elem *tile, int tid) {
+        st.template store<LD>(tile, tid);
+    }
+};
 
 // ---------------------------------------------------------------------------
 // dQ: per workgroup BR = 32*WAVES query rows (one 32-row block per wave, each
@@ -113,9 +141,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     constexpr int KPL = Tr::KPL;
     constexpr int KSTEP = 2 * KPL;
     constexpr int VEC = vec_elems<DT>();
-    constexpr int LDK = D + VEC;
+    using Tl = BwdTile<DT, D>;
     constexpr int LDT = BC + 4;          // float32 transposed K copy
-    constexpr int KS = BC * LDK;
+    constexpr int KS = BC * Tl::LD;
     constexpr int TSZ = TR ? 1 : D * LDT;
     constexpr int NKB = BC / 32;
     constexpr int NDB = D / 32;
@@ -169,8 +197,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
         if constexpr (!TR) ktst.load(K + koff + (int64_t)row0 * D, n_k - row0, tid);
     };
     auto store = [&](int stage) {
-        kst.template store<LDK>(Ks + stage * KS, tid);
-        vst.template store<LDK>(Vs + stage * KS, tid);
+        Tl::store(kst, Ks + stage * KS, tid);
+        Tl::store(vst, Vs + stage * KS, tid);
         if constexpr (!TR) ktst.template store_transposed<LDT>(Kt + stage * TSZ, tid);
     };
 
@@ -188,12 +216,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             f32x16 s = zero16(), dp = zero16();
-            const elem *krow = kt + (32 * kb + col) * LDK;
-            const elem *vrow = vt + (32 * kb + col) * LDK;
 #pragma unroll
             for (int t = 0; t < TS; ++t) {
-                s = Tr::mfma(ld_row_frag<DT>(krow, t, h), qf[t], s);
-                dp = Tr::mfma(ld_row_frag<DT>(vrow, t, h), df[t], dp);
+                s = Tr::mfma(Tl::row(kt, 32 * kb + col, t, h), qf[t], s);
+                dp = Tr::mfma(Tl::row(vt, 32 * kb + col, t, h), df[t], dp);
             }
 #pragma unroll
             for (int c = 0; c < 16; ++c) {
@@ -205,7 +231,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
                 const frag dsf = c_to_frag<DT>(s, t);
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
-                    acc[db] = Tr::mfma(ld_trans_frag<DT, LDK, LDT>(kt, ktt, kb, t, db, lane), dsf, acc[db]);
+                    acc[db] = Tr::mfma(Tl::template trans<LDT>(kt, ktt, kb, t, db, lane), dsf, acc[db]);
             }
         }
         if (it + 1 < ntiles) {
@@ -226,13 +252,15 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 
 // ---------------------------------------------------------------------------
 // dK, dV: per workgroup BKV = 32*WAVES key rows, wave w owning keys
-// 32w..32w+31 with their K and V rows in registers (B operands). Query tiles
+// 32w..32w+31 as B operands: K rows in registers, V rows in LDS for 16-bit
+// types (read once per 32-query block; that keeps a wave within 256 VGPRs,
+// i.e. two waves per SIMD) and in registers for float32. Query tiles
 // of BQ rows: Q and dO row-major in LDS (A operands of S = Q K^T and
 // dP = dO V^T, and via transposing reads of dK^T += Q^T dS and
 // dV^T += dO^T P), plus lse*log2e and delta. C blocks: rows = queries,
 // column = key; lse and delta vary along a lane's registers.
 template <Dt DT, int D, int BQ, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void dkdv_kernel(
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_kernel(
     const typename Traits<DT>::elem *__restrict__ Q, const typename Traits<DT>::elem *__restrict__ K,
     const typename Traits<DT>::elem *__restrict__ V, const typename Traits<DT>::elem *__restrict__ dO,
     const float *__restrict__ LSE, const float *__restrict__ Delta, typename Traits<DT>::elem *__restrict__ dK,
@@ -247,9 +275,9 @@ __global__ __launch_bounds__(WAVES * 64) void dkdv_kernel(
     constexpr int KPL = Tr::KPL;
     constexpr int KSTEP = 2 * KPL;
     constexpr int VEC = vec_elems<DT>();
-    constexpr int LDQ = D + VEC;
-    constexpr int LDT = BQ + 4;
-    constexpr int QS = BQ * LDQ;
+    using Tl = BwdTile<DT, D>;
+    constexpr int LDT = BQ + 4;          // float32 transposed copies
+    constexpr int QS = BQ * Tl::LD;
     constexpr int TSZ = TR ? 1 : D * LDT;
     constexpr int NQB = BQ / 32;
     constexpr int NDB = D / 32;
@@ -263,6 +291,8 @@ __global__ __launch_bounds__(WAVES * 64) void dkdv_kernel(
     __shared__ __attribute__((aligned(16))) elem Dt_[2 * TSZ];
     __shared__ __attribute__((aligned(16))) float Ls[2 * BQ];
     __shared__ __attribute__((aligned(16))) float Dl[2 * BQ];
+    constexpr bool VLDS = TR;
+    __shared__ __attribute__((aligned(16))) elem Vk[VLDS ? BKV * Tl::LD : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, col = lane & 31;
@@ -273,19 +303,34 @@ __global__ __launch_bounds__(WAVES * 64) void dkdv_kernel(
     const int64_t koff = (int64_t)bh * n_k * D;
     const int64_t loff = (int64_t)bh * n_q;
 
-    frag kf[TS], vf[TS];
+    frag kf[TS], vf[VLDS ? 1 : TS];
     if (krow < n_k) {
         const elem *kp = K + koff + (int64_t)krow * D;
-        const elem *vp = V + koff + (int64_t)krow * D;
 #pragma unroll
-        for (int t = 0; t < TS; ++t) {
-            kf[t] = ld_row_frag<DT>(kp, t, h);
-            vf[t] = ld_row_frag<DT>(vp, t, h);
+        for (int t = 0; t < TS; ++t) kf[t] = ld_row_frag<DT>(kp, t, h);
+        if constexpr (!VLDS) {
+            const elem *vp = V + koff + (int64_t)krow * D;
+#pragma unroll
+            for (int t = 0; t < TS; ++t) vf[t] = ld_row_frag<DT>(vp, t, h);
         }
     } else {
 #pragma unroll
-        for (int t = 0; t < TS; ++t) kf[t] = vf[t] = zero_frag_b<DT>();
+        for (int t = 0; t < TS; ++t) kf[t] = zero_frag_b<DT>();
+        if constexpr (!VLDS) {
+#pragma unroll
+            for (int t = 0; t < TS; ++t) vf[t] = zero_frag_b<DT>();
+        }
     }
+    if constexpr (VLDS) {
+        // this workgroup's V rows (rows past n_k read as zero)
+        const __amdgpu_buffer_rsrc_t vrs =
+            make_rsrc(V + koff, (uint32_t)n_k * D * (uint32_t)sizeof(elem));
+        RowStage<DT, BKV, D, NT> vst;
+        vst.load(vrs, kblk * BKV, tid);
+        Tl::store(vst, Vk, tid);
+        // made visible by the barrier after the first query tile is staged
+    }
+    const elem *vkrow = Vk + (wave * 32 + col) * Tl::LD;
 
     f32x16 accK[NDB], accV[NDB];
 #pragma unroll
@@ -315,8 +360,8 @@ __global__ __launch_bounds__(WAVES * 64) void dkdv_kernel(
         }
     };
     auto store = [&](int stage) {
-        qst.template store<LDQ>(Qs + stage * QS, tid);
-        dst.template store<LDQ>(Ds + stage * QS, tid);
+        Tl::store(qst, Qs + stage * QS, tid);
+        Tl::store(dst, Ds + stage * QS, tid);
         if (tid < BQ) {
             Ls[stage * BQ + tid] = lreg * kLog2e;
             Dl[stage * BQ + tid] = dreg;
@@ -344,12 +389,13 @@ __global__ __launch_bounds__(WAVES * 64) void dkdv_kernel(
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
             f32x16 s = zero16(), dp = zero16();
-            const elem *qrow = qt + (32 * qb + col) * LDQ;
-            const elem *drow = dt + (32 * qb + col) * LDQ;
 #pragma unroll
             for (int t = 0; t < TS; ++t) {
-                s = Tr::mfma(ld_row_frag<DT>(qrow, t, h), kf[t], s);
-                dp = Tr::mfma(ld_row_frag<DT>(drow, t, h), vf[t], dp);
+                s = Tr::mfma(Tl::row(qt, 32 * qb + col, t, h), kf[t], s);
+                if constexpr (VLDS)
+                    dp = Tr::mfma(Tl::row(dt, 32 * qb + col, t, h), ld_row_frag<DT>(vkrow, t, h), dp);
+                else
+                    dp = Tr::mfma(Tl::row(dt, 32 * qb + col, t, h), vf[t], dp);
             }
             // p into s, dS into dp
 #pragma unroll
@@ -372,8 +418,8 @@ __global__ __launch_bounds__(WAVES * 64) void dkdv_kernel(
                 const frag dsf = c_to_frag<DT>(dp, t);
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    accV[db] = Tr::mfma(ld_trans_frag<DT, LDQ, LDT>(dt, dtt, qb, t, db, lane), pf, accV[db]);
-                    accK[db] = Tr::mfma(ld_trans_frag<DT, LDQ, LDT>(qt, qtt, qb, t, db, lane), dsf, accK[db]);
+                    accV[db] = Tr::mfma(Tl::template trans<LDT>(dt, dtt, qb, t, db, lane), pf, accV[db]);
+                    accK[db] = Tr::mfma(Tl::template trans<LDT>(qt, qtt, qb, t, db, lane), dsf, accK[db]);
                 }
             }
         }
@@ -433,13 +479,12 @@ static hipError_t dq_dispatch(const void *q, const void *k, const void *v, const
     return dq_launch<DT, D, 2>(q, k, v, d_o, lse, delta, dq, s, stream);
 }
 
-template <Dt DT, int D>
-static hipError_t dkdv_dispatch(const void *q, const void *k, const void *v, const void *d_o, const float *lse,
-                                const float *delta, void *dk, void *dv, const AttnShape &s, hipStream_t stream) {
+template <Dt DT, int D, int WAVES>
+static hipError_t dkdv_launch(const void *q, const void *k, const void *v, const void *d_o, const float *lse,
+                              const float *delta, void *dk, void *dv, const AttnShape &s, hipStream_t stream) {
     using elem = typename Traits<DT>::elem;
-    constexpr int WAVES = 4, BKV = 32 * WAVES;
-    constexpr int BQ = (sizeof(elem) == 4 && D == 128) ? 32 : 64;
-    static_assert(BKV == kDkdvKeysPerBlock, "key block");
+    constexpr int BKV = 32 * WAVES;
+    constexpr int BQ = 32;  // one 32-query block per tile keeps a wave within 256 VGPRs
     const int nkb = (s.n_k + BKV - 1) / BKV;
     const int total = (int)(s.bh * nkb);
     const float scale_log2 = (float)((double)s.scale * 1.4426950408889634);
@@ -447,6 +492,17 @@ static hipError_t dkdv_dispatch(const void *q, const void *k, const void *v, con
                        (const elem *)q, (const elem *)k, (const elem *)v, (const elem *)d_o, lse, delta,
                        (elem *)dk, (elem *)dv, s.n_q, s.n_k, nkb, total, scale_log2, s.scale);
     return hipGetLastError();
+}
+
+// Workgroup size by problem size, as for the forward (key rows here).
+template <Dt DT, int D>
+static hipError_t dkdv_dispatch(const void *q, const void *k, const void *v, const void *d_o, const float *lse,
+                                const float *delta, void *dk, void *dv, const AttnShape &s, hipStream_t stream) {
+    constexpr int64_t kCus = 256;
+    if (s.bh * ((s.n_k + 255) / 256) >= 2 * kCus)
+        return dkdv_launch<DT, D, 8>(q, k, v, d_o, lse, delta, dk, dv, s, stream);
+    if (s.bh * ((s.n_k + 127) / 128) >= kCus) return dkdv_launch<DT, D, 4>(q, k, v, d_o, lse, delta, dk, dv, s, stream);
+    return dkdv_launch<DT, D, 2>(q, k, v, d_o, lse, delta, dk, dv, s, stream);
 }
 
 #define FA2_DISPATCH_DIM(FN, DT, HD, ...)                         \

@@ -51,6 +51,17 @@ __device__ __forceinline__ void store4(typename Traits<DT>::elem *dst, const f32
     }
 }
 
+// V tile row stride. 16-bit types: row-major, read only by
+// ds_read_b64_tr_b16, which serves 4 rows x 64 bytes per cycle; rows whose
+// starts are 64 bytes apart modulo 256 keep those in distinct banks (64-byte
+// pad from D = 64 up; D = 32 rows are 64 bytes already). float32: the tile
+// is stored transposed (keys contiguous).
+template <Dt DT, int D, int BC>
+constexpr int fwd_ldv() {
+    if constexpr (sizeof(typename Traits<DT>::elem) == 2) return D >= 64 ? D + 32 : D;
+    else return BC + 4;
+}
+
 // One key tile of the forward for one wave: scores, online softmax with lazy
 // rescaling, and the P V accumulation. MASK: the tile is the ragged last one
 // and keys at or beyond kvalid do not exist (probability 0).
@@ -67,7 +78,7 @@ __device__ __forceinline__ void fwd_tile(const typename Traits<DT>::elem *kt, co
     constexpr int KSTEP = 2 * KPL;
     constexpr int VEC = vec_elems<DT>();
     constexpr int LDK = D + VEC;
-    constexpr int LDV = TR ? D + 2 * VEC : BC + 4;
+    constexpr int LDV = fwd_ldv<DT, D, BC>();
     constexpr int NKB = BC / 32;
     constexpr int NDB = D / 32;
     constexpr int TS = D / KSTEP;
@@ -158,8 +169,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     constexpr int KSTEP = 2 * KPL;
     constexpr int VEC = vec_elems<DT>();
     constexpr int LDK = D + VEC;            // K tile: row-major, 16-byte pad
-    constexpr int LDV = TR ? D + 2 * VEC    // V tile: row-major, 32-byte pad
-                           : BC + 4;        //   (f32: transposed, keys contiguous)
+    constexpr int LDV = fwd_ldv<DT, D, BC>();
     constexpr int KS = BC * LDK;            // elements per K stage
     constexpr int VS = TR ? BC * LDV : D * LDV;
     constexpr int NKB = BC / 32;            // 32-key blocks per tile

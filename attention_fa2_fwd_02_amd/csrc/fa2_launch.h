@@ -41,6 +41,6 @@ hipError_t launch_psa_merge(int dt, const void *lo, const void *hi, void *out, c
 // Smallest query rows per forward / dq workgroup and key rows per dkdv
 // workgroup (the ABI checks that the 1-D grids fit in int32).
 constexpr int kFwdRowsPerBlock = 64;
-constexpr int kDkdvKeysPerBlock = 128;
+constexpr int kDkdvKeysPerBlock = 64;
 
 }  // namespace fa2mi
