@@ -46,6 +46,9 @@ def _parse():
     ap.add_argument("--no-legs", action="store_true", help="skip the other-shape legs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0, help="oracle sample heads (0: one per thread)")
+    ap.add_argument("--only", choices=["main", "c3_fwd", "c4", "c5", "c2"], default=None,
+                    help="run just the main step or just one leg (for profiling one workload); prints no JSON "
+                         "line unless it is the main step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run a plain 1 GiB device copy three times (reference kernel "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -89,8 +92,10 @@ def _traffic(kernel: str):
     try:
         data = json.loads(f.read_text())
         ent = data["kernels"][kernel]
-        src = ROOT / ent["source"]
-        if hashlib.sha256(src.read_bytes()).hexdigest() != ent["source_sha256"]:
+        h = hashlib.sha256()
+        for src in ent["source"]:
+            h.update((ROOT / src).read_bytes())
+        if h.hexdigest() != ent["source_sha256"]:
             return None
         return ent["fetch_bytes"] + ent["write_bytes"]
     except (KeyError, ValueError, OSError):
@@ -120,6 +125,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
+    if args.only not in (None, "main"):
+        print(json.dumps({"leg": args.only, **_legs(torch, fa2, workloads, dev, only=args.only)[args.only]}))
+        return
 
     w3, w5 = workloads.C3, workloads.C5
     x = workloads.attn_inputs(w3, device=dev, with_do=True)
@@ -194,13 +202,13 @@ def main():
         del src, dst
 
     legs = {}
-    if not args.no_legs:
+    if not args.no_legs and args.only is None:
         del x, q, k, v, do, o, lse, delta, dq, dk, dv
         torch.cuda.empty_cache()
         legs = _legs(torch, fa2, workloads, dev)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.only is None:
         cpu = _cpu_baseline(w3, args.cpu_heads)
 
     out = {
@@ -248,8 +256,20 @@ def _time_fn(torch, fn, reps, warm=3, flush=None):
     return ts[len(ts) // 2]
 
 
-def _legs(torch, fa2, workloads, dev):
+def _legs(torch, fa2, workloads, dev, only=None):
     legs = {}
+    if only in (None, "c3_fwd"):
+        _leg_c3(torch, fa2, workloads, dev, legs)
+    if only in (None, "c4"):
+        _leg_c4(torch, fa2, workloads, dev, legs)
+    if only in (None, "c5"):
+        _leg_c5(torch, fa2, workloads, dev, legs)
+    if only in (None, "c2"):
+        _leg_c2(torch, fa2, workloads, dev, legs)
+    return legs
+
+
+def _leg_c3(torch, fa2, workloads, dev, legs):
     # forward alone at the LLM shape
     w3 = workloads.C3
     x = workloads.attn_inputs(w3, device=dev)
@@ -262,18 +282,22 @@ def _legs(torch, fa2, workloads, dev):
     torch.cuda.empty_cache()
     print(f"[bench] leg c3_fwd {legs['c3_fwd']}", file=sys.stderr, flush=True)
 
+
+def _leg_c4(torch, fa2, workloads, dev, legs):
     w4 = workloads.C4
     x = workloads.attn_inputs(w4, device=dev)
     o = torch.empty_like(x["q"])
     lse = torch.empty((w4.bh, w4.n_q), dtype=torch.float32, device=dev)
     ms = _time_fn(torch, lambda: fa2.fa2_fwd(x["q"], x["k"], x["v"], w4.scale, o, lse), 10)
     tf = w4.fwd_flops() / (ms * 1e-3) / 1e12
-    legs["c4_xattn_fwd"] = {"ms": round(ms, 4), "tflops": round(tf, 1),
+    legs["c4"] = {"ms": round(ms, 4), "tflops": round(tf, 1),
                             "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
     del x, o, lse
     torch.cuda.empty_cache()
-    print(f"[bench] leg c4 {legs['c4_xattn_fwd']}", file=sys.stderr, flush=True)
+    print(f"[bench] leg c4 {legs['c4']}", file=sys.stderr, flush=True)
 
+
+def _leg_c5(torch, fa2, workloads, dev, legs):
     w5 = workloads.C5
     x = workloads.attn_inputs(w5, device=dev)
     o, lse = fa2.fa2_fwd(x["q"], x["k"], x["v"], w5.scale)
@@ -287,12 +311,14 @@ def _legs(torch, fa2, workloads, dev):
 
     ms = _time_fn(torch, bwd, 10)
     tf = w5.bwd_flops() / (ms * 1e-3) / 1e12
-    legs["c5_bwd"] = {"ms": round(ms, 4), "tflops_counted": round(tf, 1),
+    legs["c5"] = {"ms": round(ms, 4), "tflops_counted": round(tf, 1),
                       "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
     del x, o, lse, delta, dq, dk, dv
     torch.cuda.empty_cache()
-    print(f"[bench] leg c5 {legs['c5_bwd']}", file=sys.stderr, flush=True)
+    print(f"[bench] leg c5 {legs['c5']}", file=sys.stderr, flush=True)
 
+
+def _leg_c2(torch, fa2, workloads, dev, legs):
     w2 = workloads.C2
     qkv = workloads.psa_inputs(w2, device=dev)
     ws = {}
@@ -303,7 +329,7 @@ def _legs(torch, fa2, workloads, dev):
     flush = _flush_buffer(torch)
     cold = _time_fn(torch, lambda: fa2.psa_block(qkv, w2.num_heads, w2.key_dim, ws), 20, flush=flush)
     del flush
-    legs["c2_psa_block"] = {
+    legs["c2"] = {
         "us_per_call_warm": round(warm * 1e3, 2), "us_per_call_cold": round(cold * 1e3, 2),
         "bytes": total_bytes,
         "gbs_warm": round(total_bytes / (warm * 1e-3) / 1e9, 1),
@@ -311,8 +337,7 @@ def _legs(torch, fa2, workloads, dev):
         "frac_hbm_cold": round(total_bytes / (cold * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "attn_tflops_warm": round(w2.attn_flops() / (warm * 1e-3) / 1e12, 2),
     }
-    print(f"[bench] leg c2 {legs['c2_psa_block']}", file=sys.stderr, flush=True)
-    return legs
+    print(f"[bench] leg c2 {legs['c2']}", file=sys.stderr, flush=True)
 
 
 def _cpu_baseline(w, heads_arg):
