@@ -10,7 +10,8 @@ every function raises if the library is missing or the tensors are not on a
 GPU.
 
 Entry points (same names as the C ABI):
-  fa2_fwd, fa2_bwd_delta, fa2_bwd_dq, fa2_bwd_dkdv, psa_pack_qkv, psa_merge_attn
+  fa2_fwd, fa2_bwd_delta, fa2_bwd_dq, fa2_bwd_dkdv, psa_pack_qkv, psa_merge_attn,
+  psa_attn_fused
 Compositions of them:
   attention_fwd (= fa2_fwd), attention_bwd (delta -> dkdv -> dq),
   psa_block (pack -> fa2_fwd on V_lo -> fa2_fwd on V_hi -> merge)
@@ -25,7 +26,7 @@ from . import _lib
 from ._lib import FA2_BF16, FA2_F16, FA2_F32, Fa2Error, library_path, load  # noqa: F401
 
 __all__ = [
-    "fa2_fwd", "fa2_bwd_delta", "fa2_bwd_dq", "fa2_bwd_dkdv", "psa_pack_qkv", "psa_merge_attn",
+    "fa2_fwd", "fa2_bwd_delta", "fa2_bwd_dq", "fa2_bwd_dkdv", "psa_pack_qkv", "psa_merge_attn", "psa_attn_fused",
     "attention_fwd", "attention_bwd", "psa_block", "Fa2Error", "load", "library_path",
 ]
 
@@ -196,3 +197,23 @@ def psa_block(qkv, num_heads: int, key_dim: int, workspace: dict | None = None):
     fa2_fwd(packed[0], packed[1], packed[2], scale, o[0], lse)
     fa2_fwd(packed[0], packed[1], packed[3], scale, o[1], lse)
     return psa_merge_attn(o[0], o[1], b, num_heads, h, w, ws["out"])
+
+
+def psa_attn_fused(qkv, num_heads: int, key_dim: int, out=None, lse=None):
+    """The PSA attention block in one kernel: qkv [B, nh*4*kd, H, W] ->
+    out [B, nh*2*kd, H, W] (scale 1/sqrt(kd)). Pass lse ([B*nh, H*W] float32)
+    to receive the log-sum-exp. Returns out."""
+    _check("qkv", qkv)
+    b, ch, h, w = qkv.shape
+    if ch != num_heads * 4 * key_dim:
+        raise ValueError(f"qkv has {ch} channels, expected num_heads*4*key_dim = {num_heads * 4 * key_dim}")
+    if out is None:
+        out = torch.empty((b, num_heads * 2 * key_dim, h, w), dtype=qkv.dtype, device=qkv.device)
+    _check("out", out, qkv.dtype, (b, num_heads * 2 * key_dim, h, w), qkv.device)
+    lse_ptr = None
+    if lse is not None:
+        _check("lse", lse, torch.float32, (b * num_heads, h * w), qkv.device)
+        lse_ptr = lse.data_ptr()
+    _lib.call("psa_attn_fused", _dtype_code(qkv), qkv.data_ptr(), out.data_ptr(), lse_ptr, b, num_heads, key_dim,
+              h, w, _stream(qkv.device))
+    return out

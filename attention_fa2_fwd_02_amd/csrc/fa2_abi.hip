@@ -169,4 +169,19 @@ fa2_status psa_merge_attn(fa2_dtype dt, const void *o_lo, const void *o_hi, void
     return launched(fn, fa2mi::launch_psa_merge((int)dt, o_lo, o_hi, out, s, (hipStream_t)stream));
 }
 
+fa2_status psa_attn_fused(fa2_dtype dt, const void *qkv, void *out, float *lse, int32_t batch,
+                          int32_t num_heads, int32_t key_dim, int32_t h, int32_t w, void *stream) {
+    static const char fn[] = "psa_attn_fused";
+    fa2_status st = check_psa(fn, dt, batch, num_heads, key_dim, h, w);
+    if (st != FA2_OK) return st;
+    if (dt == FA2_F32) return fail(FA2_ERR_UNSUPPORTED, fn, "dtype must be F16 or BF16");
+    if (key_dim != 32 && key_dim != 64) return fail(FA2_ERR_UNSUPPORTED, fn, "key_dim must be 32 or 64");
+    REQUIRE_PTR(fn, qkv);
+    REQUIRE_PTR(fn, out);
+    if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+        return fail(FA2_ERR_INVALID_ARG, fn, "lse is not 4-byte aligned");
+    const fa2mi::PsaShape s{batch, num_heads, key_dim, h * w};
+    return launched(fn, fa2mi::launch_psa_fused((int)dt, qkv, out, lse, s, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -256,6 +256,21 @@ def _time_fn(torch, fn, reps, warm=3, flush=None):
     return ts[len(ts) // 2]
 
 
+def _time_batch(torch, fn, calls, warm=3):
+    """Average time per call of `calls` back-to-back calls between two events
+    (launch latency overlapped, as in a stream of blocks)."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(calls):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / calls
+
+
 def _legs(torch, fa2, workloads, dev, only=None):
     legs = {}
     if only in (None, "c3_fwd"):
@@ -329,7 +344,22 @@ def _leg_c2(torch, fa2, workloads, dev, legs):
     flush = _flush_buffer(torch)
     cold = _time_fn(torch, lambda: fa2.psa_block(qkv, w2.num_heads, w2.key_dim, ws), 20, flush=flush)
     del flush
+    out_f = torch.empty((w2.batch, w2.out_channels, w2.h, w2.w), dtype=w2.torch_dtype, device=dev)
+    fused_warm = _time_fn(torch, lambda: fa2.psa_attn_fused(qkv, w2.num_heads, w2.key_dim, out_f), 50)
+    flush = _flush_buffer(torch)
+    fused_cold = _time_fn(torch, lambda: fa2.psa_attn_fused(qkv, w2.num_heads, w2.key_dim, out_f), 20, flush=flush)
+    del flush
+    fused_bytes = byts["fused"]  # qkv read once, out written once
+    fused_stream = _time_batch(torch, lambda: fa2.psa_attn_fused(qkv, w2.num_heads, w2.key_dim, out_f), 200)
+    block_stream = _time_batch(torch, lambda: fa2.psa_block(qkv, w2.num_heads, w2.key_dim, ws), 200)
     legs["c2"] = {
+        "fused_us_per_call_stream": round(fused_stream * 1e3, 2),
+        "block_us_per_call_stream": round(block_stream * 1e3, 2),
+        "fused_gbs_stream": round(fused_bytes / (fused_stream * 1e-3) / 1e9, 1),
+        "fused_us_per_call_warm": round(fused_warm * 1e3, 2), "fused_us_per_call_cold": round(fused_cold * 1e3, 2),
+        "fused_bytes": fused_bytes,
+        "fused_gbs_cold": round(fused_bytes / (fused_cold * 1e-3) / 1e9, 1),
+        "fused_frac_hbm_cold": round(fused_bytes / (fused_cold * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "us_per_call_warm": round(warm * 1e3, 2), "us_per_call_cold": round(cold * 1e3, 2),
         "bytes": total_bytes,
         "gbs_warm": round(total_bytes / (warm * 1e-3) / 1e9, 1),

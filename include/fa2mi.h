@@ -137,6 +137,23 @@ fa2_status psa_merge_attn(fa2_dtype dt, const void *o_lo, const void *o_hi, void
                           int32_t batch, int32_t num_heads, int32_t key_dim, int32_t h, int32_t w,
                           void *stream);
 
+/*
+ * Fused PSA attention forward (vision_rs psa.rs: module doc, "psa_pack_qkv",
+ * "psa_merge_attn_nchw" and "FlashAttn2PsaRuntimeOp"): the result of
+ * psa_pack_qkv, fa2_fwd on (Q, K, V_lo), fa2_fwd on (Q, K, V_hi) and
+ * psa_merge_attn, with scale 1/sqrt(key_dim) as that runtime op fixes it,
+ * in one kernel: Q, K and V are read straight from the NCHW qkv activation
+ * [batch, num_heads*4*key_dim, h, w] and the output is written straight to
+ * NCHW out [batch, num_heads*2*key_dim, h, w]. The two value halves share
+ * one probability matrix, so attention runs once with value width
+ * 2*key_dim. lse, if not NULL, receives the [batch*num_heads, h*w] float32
+ * natural-log LSE (the same for both halves). dt is F16 or BF16 and key_dim
+ * 32 or 64 (others: FA2_ERR_UNSUPPORTED); lse must be 4-byte aligned.
+ */
+fa2_status psa_attn_fused(fa2_dtype dt, const void *qkv, void *out, float *lse,
+                          int32_t batch, int32_t num_heads, int32_t key_dim, int32_t h, int32_t w,
+                          void *stream);
+
 #ifdef __cplusplus
 }
 #endif

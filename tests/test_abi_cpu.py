@@ -78,6 +78,11 @@ def test_bwd_and_psa_reject_invalid_arguments():
     assert lib.psa_merge_attn(1, A, A, MIS, 16, 4, 32, 20, 20, None) == INVALID
     assert lib.psa_merge_attn(5, A, A, A, 16, 4, 32, 20, 20, None) == INVALID
     assert b"psa_merge_attn" in lib.fa2_last_error()
+    assert lib.psa_attn_fused(0, A, A, None, 16, 4, 32, 20, 20, None) == UNSUPPORTED   # f32
+    assert lib.psa_attn_fused(1, A, A, None, 16, 4, 128, 20, 20, None) == UNSUPPORTED  # key_dim 128
+    assert lib.psa_attn_fused(1, A, None, None, 16, 4, 32, 20, 20, None) == INVALID
+    assert lib.psa_attn_fused(2, A, A, A + 2, 16, 4, 32, 20, 20, None) == INVALID     # lse misaligned
+    assert lib.psa_attn_fused(2, A, A, A, 16, 4, 32, 0, 20, None) == INVALID
 
 
 def test_binding_refuses_host_tensors():

@@ -259,3 +259,42 @@ def test_bwd_deterministic():
     torch.cuda.synchronize()
     for u, v_ in zip(a, b):
         assert torch.equal(u, v_)
+
+
+# ---------------------------------------------------------------------------
+# Fused PSA forward (one kernel, NCHW in and out)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("kd,b,nh,h,w", [(32, 16, 4, 20, 20), (32, 2, 3, 5, 7), (64, 2, 2, 9, 9),
+                                         (32, 1, 1, 1, 1), (64, 3, 1, 16, 24), (32, 2, 2, 13, 11)])
+def test_psa_attn_fused(dt, kd, b, nh, h, w):
+    dtype = DTYPES[dt]
+    case = f"psa fused {dt} kd={kd} b={b} nh={nh} h={h} w={w}"
+    print(case, flush=True)
+    wl = workloads.PsaWorkload("case", b, nh, kd, h, w, dt, seed=kd + b + h * w)
+    qkv = workloads.psa_inputs(wl, device=DEV)
+    lse = torch.empty((b * nh, h * w), dtype=torch.float32, device=DEV)
+    out = fa2.psa_attn_fused(qkv, nh, kd, lse=lse)
+    torch.cuda.synchronize()
+    want = oracle.psa_block(qkv, nh, kd)
+    _err("out", _np(out), want, 2e-2, case)
+    packed = oracle.psa_pack(qkv, nh, kd)
+    pk = torch.from_numpy(packed.view(np.int16)).view(dtype)
+    _, lse_ref = oracle.attention_fwd(pk[0], pk[1], pk[2], 1 / math.sqrt(kd))
+    _err("LSE", _np(lse), lse_ref, 2e-2, case)
+    # the four-launch block computes the same thing
+    blk = fa2.psa_block(qkv, nh, kd)
+    torch.cuda.synchronize()
+    _err("vs block", _np(out), _np(blk), 2e-2, case)
+
+
+def test_psa_attn_fused_no_lse_and_canary():
+    wl = workloads.C2
+    qkv = workloads.psa_inputs(wl, device=DEV)
+    n = wl.batch * wl.out_channels * wl.n
+    buf = torch.full((n + 4096,), float("nan"), dtype=torch.float16, device=DEV)
+    out = buf[:n].view(wl.batch, wl.out_channels, wl.h, wl.w)
+    fa2.psa_attn_fused(qkv, wl.num_heads, wl.key_dim, out=out)
+    torch.cuda.synchronize()
+    assert torch.isnan(buf[n:]).all() and torch.isfinite(out).all()

@@ -108,6 +108,7 @@ class PsaWorkload:
             "pack": 2 * qkv,
             "attn_each": 4 * sec + lse,
             "merge": 2 * sec + out,
+            "fused": qkv + out,
         }
 
 
