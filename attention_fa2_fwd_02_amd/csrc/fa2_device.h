@@ -236,6 +236,15 @@ struct TileStage {
 };
 
 // ---------------------------------------------------------------------------
+// Direct global -> LDS load of 16 bytes per lane (gfx950
+// global_load_lds_dwordx4): lane l of the wave writes the 16 bytes at its own
+// global address `g` to LDS at `lds_base + 16 l`; lds_base must be the same
+// for every lane of the instruction.
+__device__ __forceinline__ void load_lds16(const void *g, void *lds_base) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
 // Buffer resources: a raw buffer over one head's rows. Loads at byte offsets
 // at or past `bytes` return zero (hardware range check), which zero-fills the
 // rows of a ragged last tile without branches.

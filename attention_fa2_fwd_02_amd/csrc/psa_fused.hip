@@ -23,8 +23,69 @@
 
 namespace fa2mi {
 
+// One key tile of the fused PSA forward for one wave (K^T and V^T tiles in
+// LDS): scores, online softmax with lazy rescaling, P V. MASK: the tile is
+// the ragged last one (keys at or beyond kvalid get probability 0).
+template <Dt DT, int KD, int LDKT, int LDVT, bool MASK>
+__device__ __forceinline__ void psa_tile(const typename Traits<DT>::elem *kt, const typename Traits<DT>::elem *vt,
+                                         const typename Traits<DT>::frag (&qf)[KD / 16], f32x16 (&acc)[KD / 16],
+                                         float &m_ref, float &l_run, float scale_log2, int kvalid, int lane) {
+    using Tr = Traits<DT>;
+    using frag = typename Tr::frag;
+    constexpr int TS = KD / 16, NKB = 2, NDB = 2 * KD / 32;
+    const int h = lane >> 5, col = lane & 31;
+    f32x16 s[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = zero16();
+#pragma unroll
+    for (int t = 0; t < TS; ++t)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+            s[kb] = Tr::mfma(ld_vt_frag_tr<DT>(kt, LDKT, 16 * t, 32 * kb, lane), qf[t], s[kb]);
+    if constexpr (MASK) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int c = 0; c < 16; ++c)
+                if (32 * kb + crow(c, h) >= kvalid) s[kb][c] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int c = 0; c < 16; ++c) mx = fmaxf(mx, s[kb][c]);
+    const float mx2 = mx * scale_log2;
+    if (__any(mx2 > m_ref + kRescaleLog2)) {
+        const float m_new = fmaxf(m_ref, xhalf_max(mx2));
+        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int c = 0; c < 16; ++c) acc[db][c] *= alpha;
+        l_run *= alpha;
+        m_ref = m_new;
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][c], scale_log2, -m_ref));
+            s[kb][c] = p;
+            l_run += p;
+        }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const frag pf = c_to_frag<DT>(s[kb], t);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                acc[db] = Tr::mfma(ld_t_frag<DT>(vt + (32 * db + col) * LDVT, kb, t, h), pf, acc[db]);
+        }
+}
+
 template <Dt DT, int KD, int WAVES, bool ALIGNED>
-__global__ __launch_bounds__(WAVES * 64) void psa_fused_kernel(const typename Traits<DT>::elem *__restrict__ qkv,
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void psa_fused_kernel(const typename Traits<DT>::elem *__restrict__ qkv,
                                                                typename Traits<DT>::elem *__restrict__ out,
                                                                float *__restrict__ lse, int num_heads, int hw,
                                                                int n_qblocks, float scale_log2) {
@@ -135,68 +196,29 @@ __global__ __launch_bounds__(WAVES * 64) void psa_fused_kernel(const typename Tr
     for (int i = 0; i < NDB; ++i) acc[i] = zero16();
     float m_ref = -INFINITY, l_run = 0.f;
 
-    for (int it = 0; it < ntiles; ++it) {
+    const int nfull = hw / BC;
+    for (int it = 0; it < nfull; ++it) {
         const elem *kt = stage0 + (it & 1) * STAGE;
-        const elem *vt = kt + KSZ;
-        const int kvalid = hw - it * BC;
-        f32x16 s[NKB];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) s[kb] = zero16();
-#pragma unroll
-        for (int t = 0; t < TS; ++t)
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-                s[kb] = Tr::mfma(ld_vt_frag_tr<DT>(kt, LDKT, 16 * t, 32 * kb, lane), qf[t], s[kb]);
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                if (kvalid < BC && 32 * kb + crow(c, h) >= kvalid) s[kb][c] = -INFINITY;
-                mx = fmaxf(mx, s[kb][c]);
-            }
-        const float mx2 = mx * scale_log2;
-        if (__any(mx2 > m_ref + kRescaleLog2)) {
-            const float m_new = fmaxf(m_ref, xhalf_max(mx2));
-            const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int c = 0; c < 16; ++c) acc[db][c] *= alpha;
-            l_run *= alpha;
-            m_ref = m_new;
-        }
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][c], scale_log2, -m_ref));
-                s[kb][c] = p;
-                l_run += p;
-            }
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const frag pf = c_to_frag<DT>(s[kb], t);
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    acc[db] = Tr::mfma(ld_t_frag<DT>(vt + (32 * db + col) * LDVT, kb, t, h), pf, acc[db]);
-            }
+        psa_tile<DT, KD, LDKT, LDVT, false>(kt, kt + KSZ, qf, acc, m_ref, l_run, scale_log2, BC, lane);
         if (it + 1 < ntiles) {
             store_tile(stage0 + ((it + 1) & 1) * STAGE);
             if (it + 2 < ntiles) load_tile((it + 2) * BC);
         }
         __syncthreads();
     }
+    if (nfull < ntiles) {
+        const elem *kt = stage0 + (nfull & 1) * STAGE;
+        psa_tile<DT, KD, LDKT, LDVT, true>(kt, kt + KSZ, qf, acc, m_ref, l_run, scale_log2, hw - nfull * BC, lane);
+        __syncthreads();
+    }
 
-    // epilogue: O^T / l into LDS (rows = output channels), then
-    // pixel-contiguous 16-byte stores
+    // epilogue: O^T / l into LDS (rows = output channels; the K/V stages are
+    // free after the last barrier), then pixel-contiguous 16-byte stores
     const float l_tot = xhalf_sum(l_run);
     const float inv = 1.f / l_tot;
     const int qrow = q0 + wave * 32 + col;
     if (lse != nullptr && h == 0 && qrow < hw) lse[(int64_t)bh * hw + qrow] = (m_ref + __log2f(l_tot)) * kLn2;
-    elem *Os = stage0;  // the K/V stages are free after the last barrier
+    elem *Os = stage0;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -221,6 +243,7 @@ __global__ __launch_bounds__(WAVES * 64) void psa_fused_kernel(const typename Tr
     }
 }
 
+
 template <Dt DT, int KD, int WAVES>
 static hipError_t psa_fused_launch(const void *qkv, void *out, float *lse, const PsaShape &s, hipStream_t stream) {
     using elem = typename Traits<DT>::elem;
@@ -237,12 +260,13 @@ static hipError_t psa_fused_launch(const void *qkv, void *out, float *lse, const
     return hipGetLastError();
 }
 
-// Query rows per workgroup: 128 (4 waves) when that still gives every CU a
-// workgroup, else 64.
+// Query rows per workgroup: 128 (4 waves) for long sequences with many
+// workgroups, else 64 (short sequences leave few waves per CU, and each
+// wave's serial work, not K/V staging, sets the time).
 template <Dt DT, int KD>
 static hipError_t psa_fused_dispatch(const void *qkv, void *out, float *lse, const PsaShape &s, hipStream_t stream) {
     const int64_t bh = (int64_t)s.batch * s.num_heads;
-    if (bh * ((s.hw + 127) / 128) >= 256) return psa_fused_launch<DT, KD, 4>(qkv, out, lse, s, stream);
+    if (bh * ((s.hw + 127) / 128) >= 4 * 256) return psa_fused_launch<DT, KD, 4>(qkv, out, lse, s, stream);
     return psa_fused_launch<DT, KD, 2>(qkv, out, lse, s, stream);
 }
 
