@@ -36,8 +36,11 @@ fa2_status check_attn(const char *fn, fa2_dtype dt, int64_t bh, int64_t n_q, int
     if (bh <= 0 || n_q <= 0 || n_k <= 0 || head_dim <= 0)
         return fail(FA2_ERR_INVALID_ARG, fn, "bh, n_q, n_k and head_dim must all be > 0");
     if (!good_dim(head_dim)) return fail(FA2_ERR_UNSUPPORTED, fn, "head_dim must be 32, 64 or 128");
-    if (n_q * head_dim > INT_MAX || n_k * head_dim > INT_MAX)
-        return fail(FA2_ERR_INVALID_ARG, fn, "n * head_dim exceeds 2^31 - 1 elements per head");
+    // One head's [n, head_dim] rows stay within 2 GiB, so the kernels' 32-bit
+    // byte offsets (including a tile read past the last row) cannot wrap.
+    const int64_t es = dt == FA2_F32 ? 4 : 2;
+    if ((n_q > n_k ? n_q : n_k) * head_dim * es > (int64_t(1) << 31))
+        return fail(FA2_ERR_INVALID_ARG, fn, "one head's rows exceed 2 GiB (n * head_dim * element size)");
     if (!(scale > 0.f) || scale == __builtin_inff())
         return fail(FA2_ERR_INVALID_ARG, fn, "scale must be positive and finite");
     const int64_t blocks = (grid_rows + rows_per_block - 1) / rows_per_block;

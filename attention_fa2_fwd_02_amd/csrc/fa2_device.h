@@ -267,14 +267,15 @@ struct RowStage {
     static constexpr int PER_THREAD = (PIECES + NT - 1) / NT;
     uint4 v[PER_THREAD];
 
-    // rows row0 .. row0+R-1 of the buffer (row stride D elements)
+    // rows row0 .. row0+R-1 of the buffer (row stride D elements); byte
+    // offsets are 32-bit, so the buffer plus one tile must stay below 4 GiB
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, int row0, int tid) {
 #pragma unroll
         for (int i = 0; i < PER_THREAD; ++i) {
             const int pc = tid + i * NT;
             const int row = pc / (D / VEC), cv = pc % (D / VEC);
             if (PIECES % NT == 0 || pc < PIECES)
-                v[i] = buffer_load16(rsrc, (uint32_t)(((row0 + row) * D + cv * VEC) * (int)sizeof(elem)));
+                v[i] = buffer_load16(rsrc, ((uint32_t)(row0 + row) * D + cv * VEC) * (uint32_t)sizeof(elem));
         }
     }
 

@@ -25,9 +25,11 @@
  * Errors (checked on the host before anything is enqueued; nothing is enqueued
  * when a call fails):
  *   FA2_ERR_INVALID_ARG  a NULL pointer, a pointer not 16-byte aligned, a size
- *                        <= 0, sizes whose per-head element count exceeds
- *                        2^31 - 1, a softmax scale that is not positive and
- *                        finite, or an unknown dtype;
+ *                        <= 0, one head's rows larger than 2 GiB
+ *                        (n * head_dim * element size; for the PSA calls,
+ *                        h * w * key_dim above 2^31 - 1 elements), a softmax
+ *                        scale that is not positive and finite, or an
+ *                        unknown dtype;
  *   FA2_ERR_UNSUPPORTED  a head_dim / key_dim outside {32, 64, 128};
  *   FA2_ERR_LAUNCH       the HIP runtime refused the launch.
  * fa2_last_error() returns a message for the calling thread's last failure.

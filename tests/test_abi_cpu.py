@@ -56,7 +56,9 @@ def _fwd(**kw):
     ({"d": 48}, UNSUPPORTED), ({"d": 256}, UNSUPPORTED), ({"d": 0}, INVALID),
     ({"scale": float("nan")}, INVALID), ({"scale": float("inf")}, INVALID),
     ({"scale": 0.0}, INVALID), ({"scale": -0.125}, INVALID),
-    ({"n_q": 1 << 25, "d": 128}, INVALID),          # n*d over 2^31-1 per head
+    ({"n_q": 1 << 25, "d": 128}, INVALID),          # one head's rows over 2 GiB
+    ({"n_k": (1 << 23) + 1, "d": 128}, INVALID),    # bf16 keys: 2 GiB + 256 B
+    ({"dt": 0, "n_q": (1 << 22) + 1, "d": 128}, INVALID),  # f32: 2 GiB + 512 B
     ({"bh": 1 << 40, "n_q": 1 << 20}, INVALID),     # grid over 2^31-1 workgroups
 ])
 def test_fwd_rejects_invalid_arguments(kw, code):
