@@ -10,8 +10,10 @@ on the launch stream inside the timed region.
 
 Legs measured in the same run (not part of `value`): the forward alone at
 that shape, cross-attention (BH 1024, Nq 1024, Nk 8192, D 64, K x 3), the
-backward-config step (BH 256, N 2048, D 128) and the C2PSA block (pack,
-attention twice, merge) warm and with L2/MALL flushed before each call.
+backward-config step (BH 256, N 2048, D 128), the C2PSA block (pack,
+attention twice, merge, and the fused kernel) warm and with L2/MALL flushed
+before each call, and a reference bf16 GEMM (random and constant operands)
+that shows the chip's practical dense-MFMA ceiling on random data.
 
 The CPU baseline times the fp64 oracle on a bounded sample of the same
 workload (a few heads at full sequence length) on the host cores.
@@ -46,7 +48,7 @@ def _parse():
     ap.add_argument("--no-legs", action="store_true", help="skip the other-shape legs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0, help="oracle sample heads (0: one per thread)")
-    ap.add_argument("--only", choices=["main", "c3_fwd", "c4", "c5", "c2"], default=None,
+    ap.add_argument("--only", choices=["main", "c3_fwd", "c4", "c5", "c2", "gemm_ref"], default=None,
                     help="run just the main step or just one leg (for profiling one workload); prints no JSON "
                          "line unless it is the main step")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -281,7 +283,36 @@ def _legs(torch, fa2, workloads, dev, only=None):
         _leg_c5(torch, fa2, workloads, dev, legs)
     if only in (None, "c2"):
         _leg_c2(torch, fa2, workloads, dev, legs)
+    if only in (None, "gemm_ref"):
+        _leg_gemm_ref(torch, dev, legs)
     return legs
+
+
+def _leg_gemm_ref(torch, dev, legs):
+    """Practical dense bf16 ceiling on this chip: the vendor GEMM (torch.matmul,
+    hipBLASLt) at 8192^3 with random N(0,1) operands and with constant ones.
+    Data-dependent power draw lowers the clock for random operands, so the
+    random-operand rate is the one attention kernels on real data can approach."""
+    n = 8192
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    a = torch.randn(n, n, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    b = torch.randn(n, n, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    flops = 2.0 * n * n * n
+    ms_rand = _time_fn(torch, lambda: torch.matmul(a, b, out=c), 10)
+    a.fill_(1.0)
+    b.fill_(1.0)
+    ms_const = _time_fn(torch, lambda: torch.matmul(a, b, out=c), 10)
+    tf_rand = flops / (ms_rand * 1e-3) / 1e12
+    tf_const = flops / (ms_const * 1e-3) / 1e12
+    legs["gemm_ref"] = {"shape": [n, n, n], "random_tflops": round(tf_rand, 1),
+                        "random_frac_bf16_peak": round(tf_rand / PEAK_BF16_TFLOPS, 4),
+                        "constant_tflops": round(tf_const, 1),
+                        "constant_frac_bf16_peak": round(tf_const / PEAK_BF16_TFLOPS, 4)}
+    del a, b, c
+    torch.cuda.empty_cache()
+    print(f"[bench] leg gemm_ref {legs['gemm_ref']}", file=sys.stderr, flush=True)
 
 
 def _leg_c3(torch, fa2, workloads, dev, legs):
