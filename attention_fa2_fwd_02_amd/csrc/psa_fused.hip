@@ -244,6 +244,296 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 }
 
 
+// Small feature maps (the usual C2PSA case: h*w of a few hundred pixels).
+// One workgroup per (head, 128 queries), 8 waves = 4 query sub-blocks of 32
+// x 2 key halves of NB blocks of 32 keys each. The head's whole K^T and V^T
+// (zero past h*w) and the Q^T block are fetched in one burst (V is staged in
+// LDS only after the softmax, so its latency hides behind the scores); each
+// wave keeps the scores of its key half in registers, so its softmax needs
+// one exact row max and one exp2 pass, no online rescaling, and every loop
+// has a fixed trip count (keys past h*w are masked, not skipped). The two
+// key halves of a query sub-block are merged through LDS with the
+// online-softmax combination (max, rescaled sums), each wave finishing half
+// of the value channels, and the output leaves through an LDS transpose as
+// pixel-contiguous rows.
+template <int KD, int NB>
+struct PsaSmallCfg {
+    static constexpr int KC = 2 * NB * 32;       // key capacity (h*w <= KC)
+    static constexpr int DV = 2 * KD;            // value width (V_lo | V_hi)
+    static constexpr int BR = 128;               // queries per workgroup
+    // LDS strides (elements): transposed reads of K^T and Q^T want rows an
+    // odd number of 64-byte units apart; V^T rows (8-byte reads down 32 rows)
+    // KC + 4 elements apart.
+    static constexpr int LDKT = KC + 32;
+    static constexpr int LDVT = KC + 4;
+    static constexpr int LDQ = BR + 32;
+    static constexpr int LDO = BR + 8;
+    static constexpr int KT_SZ = KD * LDKT, VT_SZ = DV * LDVT, QT_SZ = KD * LDQ;
+    // after the products the LDS holds the merge exchange (float) and then
+    // the output staging (elements)
+    static constexpr int XCH_FLOATS = 8 * 32 * (DV / 2 + 4) + 8 * 2 * 32;
+    static constexpr int OUT_ELEMS = DV * LDO;
+    static constexpr int MAIN_BYTES = 2 * (KT_SZ + VT_SZ + QT_SZ);
+    static constexpr int LDS_BYTES = MAIN_BYTES > 4 * XCH_FLOATS
+                                         ? (MAIN_BYTES > 2 * OUT_ELEMS ? MAIN_BYTES : 2 * OUT_ELEMS)
+                                         : (4 * XCH_FLOATS > 2 * OUT_ELEMS ? 4 * XCH_FLOATS : 2 * OUT_ELEMS);
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+};
+
+// Largest map each key_dim handles with this kernel (32-key blocks per half).
+template <int KD> constexpr int psa_small_max_nb() { return KD == 32 ? 7 : 4; }
+
+template <Dt DT, int KD, int NB, bool ALIGNED>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void psa_small_kernel(
+    const typename Traits<DT>::elem *__restrict__ qkv, typename Traits<DT>::elem *__restrict__ out,
+    float *__restrict__ lse, int num_heads, int hw, int n_qblocks, int total_blocks, float scale_log2) {
+    using Tr = Traits<DT>;
+    using elem = typename Tr::elem;
+    using frag = typename Tr::frag;
+    using C = PsaSmallCfg<KD, NB>;
+    static_assert(Tr::KPL == 8, "16-bit element types");
+    constexpr int NT = 512, VEC = 8, TS = KD / 16, DV = C::DV, BR = C::BR, NDB = DV / 32;
+    constexpr int LDKT = C::LDKT, LDVT = C::LDVT, LDQ = C::LDQ, LDO = C::LDO;
+    __shared__ __attribute__((aligned(16))) unsigned char lds_raw[C::LDS_BYTES];
+    elem *Kt = reinterpret_cast<elem *>(lds_raw);
+    elem *Vt = Kt + C::KT_SZ;
+    elem *Qt = Vt + C::VT_SZ;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qs = wave & 3, ks = wave >> 2;  // waves w and w+4 share a SIMD
+    const int h = lane >> 5, col = lane & 31;
+    const int blk = xcd_remap(blockIdx.x, total_blocks);
+    const int bh = blk / n_qblocks, qb = blk % n_qblocks;
+    const int b = bh / num_heads, hd = bh % num_heads;
+    const int q0 = qb * BR;
+    const int64_t plane = (int64_t)hw;
+    // the head's 4*KD channel rows (Q, K, V_lo, V_hi) are contiguous
+    const elem *qbase = qkv + ((int64_t)b * num_heads * 4 * KD + (int64_t)hd * 4 * KD) * plane;
+    elem *obase = out + ((int64_t)b * num_heads * DV + (int64_t)hd * DV) * plane;
+
+    // Loads: K^T [KD][KC] and Q^T [KD][BR] first, then V^T [DV][KC] (all zero
+    // past hw). V stays in registers while the scores and the softmax run and
+    // is staged in LDS only before the P V products.
+    constexpr int K_VECS = KD * (C::KC / VEC);
+    constexpr int Q_VECS = KD * (BR / VEC);
+    constexpr int V_VECS = DV * (C::KC / VEC);
+    constexpr int PER_KQ = (K_VECS + Q_VECS + NT - 1) / NT;
+    constexpr int PER_V = (V_VECS + NT - 1) / NT;
+    // buffer over the head's channel rows (Q, K, V_lo, V_hi are contiguous);
+    // vectors past a row's hw pixels get an offset beyond the range and read
+    // as zero
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(qbase, (uint32_t)(4 * KD * hw) * (uint32_t)sizeof(elem));
+    auto load_vec = [&](int row, int p) -> uint4 {
+        if constexpr (ALIGNED) {
+            const uint32_t off = p < hw ? ((uint32_t)row * hw + p) * (uint32_t)sizeof(elem) : 0xfffffff0u;
+            return buffer_load16(rs, off);
+        } else {
+            uint4 x = make_uint4(0, 0, 0, 0);
+            elem *e = reinterpret_cast<elem *>(&x);
+            const elem *rowp = qbase + (int64_t)row * plane;
+#pragma unroll
+            for (int k = 0; k < VEC; ++k)
+                if (p + k < hw) e[k] = rowp[p + k];
+            return x;
+        }
+    };
+    uint4 rkq[PER_KQ], rv[PER_V];
+#pragma unroll
+    for (int i = 0; i < PER_KQ; ++i) {
+        const int v = tid + i * NT;
+        if (v < K_VECS)
+            rkq[i] = load_vec(KD + v / (C::KC / VEC), (v % (C::KC / VEC)) * VEC);
+        else if (v < K_VECS + Q_VECS)
+            rkq[i] = load_vec((v - K_VECS) / (BR / VEC), q0 + ((v - K_VECS) % (BR / VEC)) * VEC);
+    }
+#pragma unroll
+    for (int i = 0; i < PER_V; ++i) {
+        const int v = tid + i * NT;
+        if (V_VECS % NT == 0 || v < V_VECS) rv[i] = load_vec(2 * KD + v / (C::KC / VEC), (v % (C::KC / VEC)) * VEC);
+    }
+#pragma unroll
+    for (int i = 0; i < PER_KQ; ++i) {
+        const int v = tid + i * NT;
+        if (v < K_VECS) {
+            *reinterpret_cast<uint4 *>(Kt + (v / (C::KC / VEC)) * LDKT + (v % (C::KC / VEC)) * VEC) = rkq[i];
+        } else if (v < K_VECS + Q_VECS) {
+            const int u = v - K_VECS;
+            *reinterpret_cast<uint4 *>(Qt + (u / (BR / VEC)) * LDQ + (u % (BR / VEC)) * VEC) = rkq[i];
+        }
+    }
+    __syncthreads();
+
+    // this wave: queries q0 + 32 qs + [0, 32), key blocks ks*NB + [0, NB)
+    const int kb0 = ks * NB;
+    const bool active = q0 + 32 * qs < hw;
+    f32x16 acc[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) acc[i] = zero16();
+    float m = -INFINITY, l_run = 0.f;
+    f32x16 s[NB];
+    if (active) {
+        frag qf[TS];
+#pragma unroll
+        for (int t = 0; t < TS; ++t) qf[t] = ld_vt_frag_tr<DT>(Qt, LDQ, 16 * t, 32 * qs, lane);
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb) {
+            s[kb] = zero16();
+#pragma unroll
+            for (int t = 0; t < TS; ++t)
+                s[kb] = Tr::mfma(ld_vt_frag_tr<DT>(Kt, LDKT, 16 * t, 32 * (kb0 + kb), lane), qf[t], s[kb]);
+        }
+        // keys past hw do not exist (probability 0); only blocks that reach
+        // past hw need the per-element test
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb) {
+            if (32 * (kb0 + kb + 1) > hw) {
+                const int limit = hw - 32 * (kb0 + kb) - 4 * h;  // first invalid crow - 4h
+#pragma unroll
+                for (int c = 0; c < 16; ++c) s[kb][c] = crow(c, 0) >= limit ? -INFINITY : s[kb][c];
+            }
+#pragma unroll
+            for (int c = 0; c < 16; ++c) mx = fmaxf(mx, s[kb][c]);
+        }
+        m = xhalf_max(mx) * scale_log2;  // exact max of this half, log2 units
+        // a half with no keys keeps m = -inf and contributes nothing
+        const float neg_m = m == -INFINITY ? 0.f : -m;
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][c], scale_log2, neg_m));
+                s[kb][c] = p;
+                l_run += p;
+            }
+    }
+    // V^T into LDS (its own region: K^T and Q^T may still be read)
+#pragma unroll
+    for (int i = 0; i < PER_V; ++i) {
+        const int v = tid + i * NT;
+        if (V_VECS % NT == 0 || v < V_VECS) {
+            elem *dst = Vt + (v / (C::KC / VEC)) * LDVT + (v % (C::KC / VEC)) * VEC;  // 8-byte aligned rows
+            reinterpret_cast<uint2 *>(dst)[0] = make_uint2(rv[i].x, rv[i].y);
+            reinterpret_cast<uint2 *>(dst)[1] = make_uint2(rv[i].z, rv[i].w);
+        }
+    }
+    __syncthreads();
+    if (active) {
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const frag pf = c_to_frag<DT>(s[kb], t);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    acc[db] = Tr::mfma(ld_t_frag<DT>(Vt + (32 * db + col) * LDVT, kb0 + kb, t, h), pf, acc[db]);
+            }
+    }
+    const float l_half = xhalf_sum(l_run);
+    __syncthreads();  // K^T / V^T no longer read: reuse the space
+
+    // Merge the two key halves. Wave (qs, ks) finishes channels
+    // [ks*DV/2, (ks+1)*DV/2) and hands the other half to its partner. The
+    // exchange is [wave][query][LDX] floats: a lane's registers 4g..4g+3 are
+    // 4 consecutive channels, moved as one 16-byte vector.
+    constexpr int LDX = DV / 2 + 4;
+    float *xch = reinterpret_cast<float *>(lds_raw);  // [wave][32][LDX]
+    float *ml = xch + 8 * 32 * LDX;                   // [wave][2][32]
+    constexpr int HDB = NDB / 2;                      // 32-channel blocks per half
+    {
+        const int give = 1 - ks;  // the half the partner finishes
+        float *dst = xch + (wave * 32 + col) * LDX;
+#pragma unroll
+        for (int j = 0; j < HDB; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x16 &a = acc[give * HDB + j];
+                *reinterpret_cast<float4 *>(dst + 32 * j + crow(4 * g, h)) =
+                    make_float4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
+            }
+        if (h == 0) {
+            ml[wave * 64 + col] = m;
+            ml[wave * 64 + 32 + col] = l_half;
+        }
+    }
+    __syncthreads();
+    const int partner = wave ^ 4;
+    const float m_o = ml[partner * 64 + col], l_o = ml[partner * 64 + 32 + col];
+    const float m_max = fmaxf(m, m_o);
+    const float a_s = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_max);
+    const float a_o = m_o == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_o - m_max);
+    const float l_tot = l_half * a_s + l_o * a_o;
+    const float inv = 1.f / l_tot;
+    const int qrow = q0 + 32 * qs + col;
+    if (lse != nullptr && ks == 0 && h == 0 && qrow < hw) lse[(int64_t)bh * hw + qrow] = (m_max + __log2f(l_tot)) * kLn2;
+    float o[HDB][16];
+    {
+        const float *src = xch + (partner * 32 + col) * LDX;
+#pragma unroll
+        for (int j = 0; j < HDB; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 x = *reinterpret_cast<const float4 *>(src + 32 * j + crow(4 * g, h));
+                const f32x16 &a = acc[ks * HDB + j];
+                o[j][4 * g] = (a[4 * g] * a_s + x.x * a_o) * inv;
+                o[j][4 * g + 1] = (a[4 * g + 1] * a_s + x.y * a_o) * inv;
+                o[j][4 * g + 2] = (a[4 * g + 2] * a_s + x.z * a_o) * inv;
+                o[j][4 * g + 3] = (a[4 * g + 3] * a_s + x.w * a_o) * inv;
+            }
+    }
+    __syncthreads();  // exchange read: reuse the space for the output rows
+    elem *Os = reinterpret_cast<elem *>(lds_raw);  // [DV][LDO]
+#pragma unroll
+    for (int j = 0; j < HDB; ++j)
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+            Os[(32 * (ks * HDB + j) + crow(c, h)) * LDO + 32 * qs + col] = static_cast<elem>(o[j][c]);
+    __syncthreads();
+    for (int i = tid; i < DV * (BR / VEC); i += NT) {
+        const int r = i / (BR / VEC), cv = i % (BR / VEC);
+        const int p = q0 + cv * VEC;
+        if (p >= hw) continue;
+        const uint4 v = *reinterpret_cast<const uint4 *>(Os + r * LDO + cv * VEC);
+        elem *dst = obase + r * plane + p;
+        if constexpr (ALIGNED) {
+            *reinterpret_cast<uint4 *>(dst) = v;
+        } else {
+            const elem *e = reinterpret_cast<const elem *>(&v);
+#pragma unroll
+            for (int k = 0; k < VEC; ++k)
+                if (p + k < hw) dst[k] = e[k];
+        }
+    }
+}
+
+template <Dt DT, int KD, int NB>
+static hipError_t psa_small_launch(const void *qkv, void *out, float *lse, const PsaShape &s, hipStream_t stream) {
+    using elem = typename Traits<DT>::elem;
+    constexpr int BR = PsaSmallCfg<KD, NB>::BR;
+    const int nqb = (s.hw + BR - 1) / BR;
+    const int grid = s.batch * s.num_heads * nqb;
+    const float scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)KD));
+    if (s.hw % 8 == 0)
+        hipLaunchKernelGGL((psa_small_kernel<DT, KD, NB, true>), dim3(grid), dim3(512), 0, stream,
+                           (const elem *)qkv, (elem *)out, lse, s.num_heads, s.hw, nqb, grid, scale_log2);
+    else
+        hipLaunchKernelGGL((psa_small_kernel<DT, KD, NB, false>), dim3(grid), dim3(512), 0, stream,
+                           (const elem *)qkv, (elem *)out, lse, s.num_heads, s.hw, nqb, grid, scale_log2);
+    return hipGetLastError();
+}
+
+// Smallest key capacity (64, 128, 256 or 448 keys) that holds the map.
+template <Dt DT, int KD>
+static hipError_t psa_small_dispatch(const void *qkv, void *out, float *lse, const PsaShape &s, hipStream_t stream) {
+    if (s.hw <= 64) return psa_small_launch<DT, KD, 1>(qkv, out, lse, s, stream);
+    if (s.hw <= 128) return psa_small_launch<DT, KD, 2>(qkv, out, lse, s, stream);
+    if constexpr (psa_small_max_nb<KD>() == 7) {
+        if (s.hw > 256) return psa_small_launch<DT, KD, 7>(qkv, out, lse, s, stream);
+    }
+    return psa_small_launch<DT, KD, 4>(qkv, out, lse, s, stream);
+}
+
 template <Dt DT, int KD, int WAVES>
 static hipError_t psa_fused_launch(const void *qkv, void *out, float *lse, const PsaShape &s, hipStream_t stream) {
     using elem = typename Traits<DT>::elem;
@@ -260,11 +550,12 @@ static hipError_t psa_fused_launch(const void *qkv, void *out, float *lse, const
     return hipGetLastError();
 }
 
-// Query rows per workgroup: 128 (4 waves) for long sequences with many
-// workgroups, else 64 (short sequences leave few waves per CU, and each
-// wave's serial work, not K/V staging, sets the time).
+// Maps of at most 64 * psa_small_max_nb pixels take the whole-head kernel above.
+// Larger ones use the tiled kernel with 128 query rows per workgroup (4
+// waves) when there are many workgroups, else 64.
 template <Dt DT, int KD>
 static hipError_t psa_fused_dispatch(const void *qkv, void *out, float *lse, const PsaShape &s, hipStream_t stream) {
+    if (s.hw <= 64 * psa_small_max_nb<KD>()) return psa_small_dispatch<DT, KD>(qkv, out, lse, s, stream);
     const int64_t bh = (int64_t)s.batch * s.num_heads;
     if (bh * ((s.hw + 127) / 128) >= 4 * 256) return psa_fused_launch<DT, KD, 4>(qkv, out, lse, s, stream);
     return psa_fused_launch<DT, KD, 2>(qkv, out, lse, s, stream);

@@ -267,7 +267,10 @@ def test_bwd_deterministic():
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 @pytest.mark.parametrize("kd,b,nh,h,w", [(32, 16, 4, 20, 20), (32, 2, 3, 5, 7), (64, 2, 2, 9, 9),
-                                         (32, 1, 1, 1, 1), (64, 3, 1, 16, 24), (32, 2, 2, 13, 11)])
+                                         (32, 1, 1, 1, 1), (64, 3, 1, 16, 24), (32, 2, 2, 13, 11),
+                                         # whole-head kernel capacity (448 / 256 pixels) and one past it
+                                         (32, 1, 2, 16, 28), (32, 1, 1, 1, 449),
+                                         (64, 1, 2, 16, 16), (64, 1, 1, 1, 257)])
 def test_psa_attn_fused(dt, kd, b, nh, h, w):
     dtype = DTYPES[dt]
     case = f"psa fused {dt} kd={kd} b={b} nh={nh} h={h} w={w}"
