@@ -254,29 +254,26 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 // has a fixed trip count (keys past h*w are masked, not skipped). The two
 // key halves of a query sub-block are merged through LDS with the
 // online-softmax combination (max, rescaled sums), each wave finishing half
-// of the value channels, and the output leaves through an LDS transpose as
-// pixel-contiguous rows.
+// of the value channels and storing them straight to the pixel rows.
 template <int KD, int NB>
 struct PsaSmallCfg {
     static constexpr int KC = 2 * NB * 32;       // key capacity (h*w <= KC)
+    // LDS rows hold KCL >= KC keys, a power of two, so that the loads map
+    // threads to (row, 16-byte column) with shifts
+    static constexpr int KCL = KC <= 64 ? 64 : KC <= 128 ? 128 : KC <= 256 ? 256 : 512;
     static constexpr int DV = 2 * KD;            // value width (V_lo | V_hi)
     static constexpr int BR = 128;               // queries per workgroup
     // LDS strides (elements): transposed reads of K^T and Q^T want rows an
     // odd number of 64-byte units apart; V^T rows (8-byte reads down 32 rows)
-    // KC + 4 elements apart.
-    static constexpr int LDKT = KC + 32;
-    static constexpr int LDVT = KC + 4;
+    // KCL + 4 elements apart.
+    static constexpr int LDKT = KCL + 32;
+    static constexpr int LDVT = KCL + 4;
     static constexpr int LDQ = BR + 32;
-    static constexpr int LDO = BR + 8;
     static constexpr int KT_SZ = KD * LDKT, VT_SZ = DV * LDVT, QT_SZ = KD * LDQ;
-    // after the products the LDS holds the merge exchange (float) and then
-    // the output staging (elements)
+    // after the products the LDS holds the merge exchange (float)
     static constexpr int XCH_FLOATS = 8 * 32 * (DV / 2 + 4) + 8 * 2 * 32;
-    static constexpr int OUT_ELEMS = DV * LDO;
     static constexpr int MAIN_BYTES = 2 * (KT_SZ + VT_SZ + QT_SZ);
-    static constexpr int LDS_BYTES = MAIN_BYTES > 4 * XCH_FLOATS
-                                         ? (MAIN_BYTES > 2 * OUT_ELEMS ? MAIN_BYTES : 2 * OUT_ELEMS)
-                                         : (4 * XCH_FLOATS > 2 * OUT_ELEMS ? 4 * XCH_FLOATS : 2 * OUT_ELEMS);
+    static constexpr int LDS_BYTES = MAIN_BYTES > 4 * XCH_FLOATS ? MAIN_BYTES : 4 * XCH_FLOATS;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
@@ -293,7 +290,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     using C = PsaSmallCfg<KD, NB>;
     static_assert(Tr::KPL == 8, "16-bit element types");
     constexpr int NT = 512, VEC = 8, TS = KD / 16, DV = C::DV, BR = C::BR, NDB = DV / 32;
-    constexpr int LDKT = C::LDKT, LDVT = C::LDVT, LDQ = C::LDQ, LDO = C::LDO;
+    constexpr int LDKT = C::LDKT, LDVT = C::LDVT, LDQ = C::LDQ;
     __shared__ __attribute__((aligned(16))) unsigned char lds_raw[C::LDS_BYTES];
     elem *Kt = reinterpret_cast<elem *>(lds_raw);
     elem *Vt = Kt + C::KT_SZ;
@@ -312,18 +309,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const elem *qbase = qkv + ((int64_t)b * num_heads * 4 * KD + (int64_t)hd * 4 * KD) * plane;
     elem *obase = out + ((int64_t)b * num_heads * DV + (int64_t)hd * DV) * plane;
 
-    // Loads: K^T [KD][KC] and Q^T [KD][BR] first, then V^T [DV][KC] (all zero
-    // past hw). V stays in registers while the scores and the softmax run and
-    // is staged in LDS only before the P V products.
-    constexpr int K_VECS = KD * (C::KC / VEC);
-    constexpr int Q_VECS = KD * (BR / VEC);
-    constexpr int V_VECS = DV * (C::KC / VEC);
-    constexpr int PER_KQ = (K_VECS + Q_VECS + NT - 1) / NT;
-    constexpr int PER_V = (V_VECS + NT - 1) / NT;
+    // Loads: Q^T [KD][BR] and K^T [KD][KCL] first, then V^T [DV][KCL] (all
+    // zero past hw). Thread tid owns 16-byte column tid % VPR of rows
+    // tid / VPR + RPP * i (VPR vectors per row, RPP rows per pass), so its
+    // offsets only step by whole rows. V stays in registers while the scores
+    // and the softmax run and is staged in LDS only before the P V products.
+    constexpr int VPR = C::KCL / VEC, RPP = NT / VPR;
+    constexpr int K_PER = (KD + RPP - 1) / RPP, V_PER = (DV + RPP - 1) / RPP;
+    constexpr int QPR = BR / VEC, Q_PER = KD * QPR / NT;  // Q^T: 16 vectors per row
+    static_assert((KD % RPP == 0 || RPP % KD == 0) && (DV % RPP == 0 || RPP % DV == 0), "load mapping");
+    static_assert(KD * QPR == Q_PER * NT, "load mapping");
     // buffer over the head's channel rows (Q, K, V_lo, V_hi are contiguous);
     // vectors past a row's hw pixels get an offset beyond the range and read
     // as zero
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(qbase, (uint32_t)(4 * KD * hw) * (uint32_t)sizeof(elem));
+    const int cvec = tid % VPR, rbase = tid / VPR;
+    const int pk = cvec * VEC;                          // this thread's key column
+    const int qr = tid / QPR, qc = (tid % QPR) * VEC;   // its Q^T vectors
     auto load_vec = [&](int row, int p) -> uint4 {
         if constexpr (ALIGNED) {
             const uint32_t off = p < hw ? ((uint32_t)row * hw + p) * (uint32_t)sizeof(elem) : 0xfffffff0u;
@@ -338,30 +340,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             return x;
         }
     };
-    uint4 rkq[PER_KQ], rv[PER_V];
+    uint4 rq[Q_PER], rk[K_PER], rv[V_PER];
 #pragma unroll
-    for (int i = 0; i < PER_KQ; ++i) {
-        const int v = tid + i * NT;
-        if (v < K_VECS)
-            rkq[i] = load_vec(KD + v / (C::KC / VEC), (v % (C::KC / VEC)) * VEC);
-        else if (v < K_VECS + Q_VECS)
-            rkq[i] = load_vec((v - K_VECS) / (BR / VEC), q0 + ((v - K_VECS) % (BR / VEC)) * VEC);
-    }
+    for (int i = 0; i < Q_PER; ++i) rq[i] = load_vec(qr + (NT / QPR) * i, q0 + qc);
 #pragma unroll
-    for (int i = 0; i < PER_V; ++i) {
-        const int v = tid + i * NT;
-        if (V_VECS % NT == 0 || v < V_VECS) rv[i] = load_vec(2 * KD + v / (C::KC / VEC), (v % (C::KC / VEC)) * VEC);
-    }
+    for (int i = 0; i < K_PER; ++i)
+        if (KD % RPP == 0 || rbase + RPP * i < KD) rk[i] = load_vec(KD + rbase + RPP * i, pk);
 #pragma unroll
-    for (int i = 0; i < PER_KQ; ++i) {
-        const int v = tid + i * NT;
-        if (v < K_VECS) {
-            *reinterpret_cast<uint4 *>(Kt + (v / (C::KC / VEC)) * LDKT + (v % (C::KC / VEC)) * VEC) = rkq[i];
-        } else if (v < K_VECS + Q_VECS) {
-            const int u = v - K_VECS;
-            *reinterpret_cast<uint4 *>(Qt + (u / (BR / VEC)) * LDQ + (u % (BR / VEC)) * VEC) = rkq[i];
-        }
-    }
+    for (int i = 0; i < V_PER; ++i)
+        if (DV % RPP == 0 || rbase + RPP * i < DV) rv[i] = load_vec(2 * KD + rbase + RPP * i, pk);
+#pragma unroll
+    for (int i = 0; i < Q_PER; ++i) *reinterpret_cast<uint4 *>(Qt + (qr + (NT / QPR) * i) * LDQ + qc) = rq[i];
+#pragma unroll
+    for (int i = 0; i < K_PER; ++i)
+        if (KD % RPP == 0 || rbase + RPP * i < KD)
+            *reinterpret_cast<uint4 *>(Kt + (rbase + RPP * i) * LDKT + pk) = rk[i];
     __syncthreads();
 
     // this wave: queries q0 + 32 qs + [0, 32), key blocks ks*NB + [0, NB)
@@ -408,12 +401,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 l_run += p;
             }
     }
-    // V^T into LDS (its own region: K^T and Q^T may still be read)
+    // V^T into LDS (its own region: K^T and Q^T may still be read); rows are
+    // 8-byte aligned
 #pragma unroll
-    for (int i = 0; i < PER_V; ++i) {
-        const int v = tid + i * NT;
-        if (V_VECS % NT == 0 || v < V_VECS) {
-            elem *dst = Vt + (v / (C::KC / VEC)) * LDVT + (v % (C::KC / VEC)) * VEC;  // 8-byte aligned rows
+    for (int i = 0; i < V_PER; ++i) {
+        if (DV % RPP == 0 || rbase + RPP * i < DV) {
+            elem *dst = Vt + (rbase + RPP * i) * LDVT + pk;
             reinterpret_cast<uint2 *>(dst)[0] = make_uint2(rv[i].x, rv[i].y);
             reinterpret_cast<uint2 *>(dst)[1] = make_uint2(rv[i].z, rv[i].w);
         }
@@ -467,8 +460,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const float inv = 1.f / l_tot;
     const int qrow = q0 + 32 * qs + col;
     if (lse != nullptr && ks == 0 && h == 0 && qrow < hw) lse[(int64_t)bh * hw + qrow] = (m_max + __log2f(l_tot)) * kLn2;
-    float o[HDB][16];
-    {
+    if (qrow < hw) {
+        // channel 32 (ks HDB + j) + crow(c, h), pixel qrow: each store
+        // instruction writes 32 consecutive pixels of two channel rows
         const float *src = xch + (partner * 32 + col) * LDX;
 #pragma unroll
         for (int j = 0; j < HDB; ++j)
@@ -476,34 +470,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int g = 0; g < 4; ++g) {
                 const float4 x = *reinterpret_cast<const float4 *>(src + 32 * j + crow(4 * g, h));
                 const f32x16 &a = acc[ks * HDB + j];
-                o[j][4 * g] = (a[4 * g] * a_s + x.x * a_o) * inv;
-                o[j][4 * g + 1] = (a[4 * g + 1] * a_s + x.y * a_o) * inv;
-                o[j][4 * g + 2] = (a[4 * g + 2] * a_s + x.z * a_o) * inv;
-                o[j][4 * g + 3] = (a[4 * g + 3] * a_s + x.w * a_o) * inv;
+                const float xo[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int chn = 32 * (ks * HDB + j) + crow(4 * g + i, h);
+                    obase[(int64_t)chn * plane + qrow] = static_cast<elem>((a[4 * g + i] * a_s + xo[i] * a_o) * inv);
+                }
             }
-    }
-    __syncthreads();  // exchange read: reuse the space for the output rows
-    elem *Os = reinterpret_cast<elem *>(lds_raw);  // [DV][LDO]
-#pragma unroll
-    for (int j = 0; j < HDB; ++j)
-#pragma unroll
-        for (int c = 0; c < 16; ++c)
-            Os[(32 * (ks * HDB + j) + crow(c, h)) * LDO + 32 * qs + col] = static_cast<elem>(o[j][c]);
-    __syncthreads();
-    for (int i = tid; i < DV * (BR / VEC); i += NT) {
-        const int r = i / (BR / VEC), cv = i % (BR / VEC);
-        const int p = q0 + cv * VEC;
-        if (p >= hw) continue;
-        const uint4 v = *reinterpret_cast<const uint4 *>(Os + r * LDO + cv * VEC);
-        elem *dst = obase + r * plane + p;
-        if constexpr (ALIGNED) {
-            *reinterpret_cast<uint4 *>(dst) = v;
-        } else {
-            const elem *e = reinterpret_cast<const elem *>(&v);
-#pragma unroll
-            for (int k = 0; k < VEC; ++k)
-                if (p + k < hw) dst[k] = e[k];
-        }
     }
 }
 
