@@ -48,6 +48,15 @@ template <> struct Traits<Dt::BF16> {
     __device__ static inline f32x16 mfma(frag a, frag b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
+    // acc + the sum of the fragment's 8 elements (fp32 accumulation)
+    __device__ static inline float sum_frag(frag f, float acc) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 0, 1), one, acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 2, 3), one, acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 4, 5), one, acc, false);
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 6, 7), one, acc, false);
+    }
 };
 
 template <> struct Traits<Dt::F16> {
@@ -57,6 +66,15 @@ template <> struct Traits<Dt::F16> {
     static constexpr int KPL = 8;
     __device__ static inline f32x16 mfma(frag a, frag b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    // acc + the sum of the fragment's 8 elements (fp32 accumulation)
+    __device__ static inline float sum_frag(frag f, float acc) {
+        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+        const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
+        acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(f, f, 0, 1), one, acc, false);
+        acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(f, f, 2, 3), one, acc, false);
+        acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(f, f, 4, 5), one, acc, false);
+        return __builtin_amdgcn_fdot2(__builtin_shufflevector(f, f, 6, 7), one, acc, false);
     }
 };
 
@@ -68,6 +86,7 @@ template <> struct Traits<Dt::F32> {
     __device__ static inline f32x16 mfma(frag a, frag b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
     }
+    __device__ static inline float sum_frag(frag f, float acc) { return acc + f; }
 };
 
 // Row of C-block register c for lane half h.

@@ -10,8 +10,8 @@
 //   2. S^T = K Q^T on MFMA: one C block per 32 keys; each lane owns one query
 //      (the C column), so a row's max needs one exchange between lane halves.
 //   3. Online softmax in the log2 domain (scale*log2(e) folded into one FMA
-//      before exp2): P = 2^(S - m), l += rowsum(P) (lane-partial sums,
-//      combined at the end). The reference max m is raised lazily: only when
+//      before exp2): P = 2^(S - m), l += rowsum(P) over P as rounded to the
+//      element type for the product (lane-partial sums, combined at the end). The reference max m is raised lazily: only when
 //      a row max exceeds it by more than kRescaleLog2, and then O and l are
 //      rescaled by 2^(m - m') as in the online-softmax recurrence.
 //   4. O^T += V^T P^T on MFMA, P fed from registers as the B operand.
@@ -130,17 +130,16 @@ __device__ __forceinline__ void fwd_tile(const typename Traits<DT>::elem *kt, co
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][c], scale_log2, neg_m));
-            s[kb][c] = p;
-            l_run += p;
-        }
-    // O^T += V^T P^T: per 16-key step, one P fragment feeds all d blocks
+        for (int c = 0; c < 16; ++c) s[kb][c] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][c], scale_log2, neg_m));
+    // O^T += V^T P^T: per 16-key step, one P fragment feeds all d blocks.
+    // l sums the probabilities as rounded for the product (so O = acc / l
+    // normalises exactly the weights applied).
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int t = 0; t < TP; ++t) {
             const frag pf = c_to_frag<DT>(s[kb], t);
+            l_run = Tr::sum_frag(pf, l_run);
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
                 frag vf;

@@ -247,8 +247,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 // Small feature maps (the usual C2PSA case: h*w of a few hundred pixels).
 // One workgroup per (head, 128 queries), 8 waves = 4 query sub-blocks of 32
 // x 2 key halves of NB blocks of 32 keys each. The head's whole K^T and V^T
-// (zero past h*w) and the Q^T block are fetched in one burst (V is staged in
-// LDS only after the softmax, so its latency hides behind the scores); each
+// (zero past h*w) and the Q^T block are fetched into LDS in one burst; each
 // wave keeps the scores of its key half in registers, so its softmax needs
 // one exact row max and one exp2 pass, no online rescaling, and every loop
 // has a fixed trip count (keys past h*w are masked, not skipped). The two
@@ -309,11 +308,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const elem *qbase = qkv + ((int64_t)b * num_heads * 4 * KD + (int64_t)hd * 4 * KD) * plane;
     elem *obase = out + ((int64_t)b * num_heads * DV + (int64_t)hd * DV) * plane;
 
-    // Loads: Q^T [KD][BR] and K^T [KD][KCL] first, then V^T [DV][KCL] (all
-    // zero past hw). Thread tid owns 16-byte column tid % VPR of rows
-    // tid / VPR + RPP * i (VPR vectors per row, RPP rows per pass), so its
-    // offsets only step by whole rows. V stays in registers while the scores
-    // and the softmax run and is staged in LDS only before the P V products.
+    // Loads: Q^T [KD][BR], K^T [KD][KCL] and V^T [DV][KCL] (all zero past
+    // hw). Thread tid owns 16-byte column tid % VPR of rows tid / VPR + RPP * i
+    // (VPR vectors per row, RPP rows per pass), so its offsets only step by
+    // whole rows.
     constexpr int VPR = C::KCL / VEC, RPP = NT / VPR;
     constexpr int K_PER = (KD + RPP - 1) / RPP, V_PER = (DV + RPP - 1) / RPP;
     constexpr int QPR = BR / VEC, Q_PER = KD * QPR / NT;  // Q^T: 16 vectors per row
@@ -355,6 +353,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int i = 0; i < K_PER; ++i)
         if (KD % RPP == 0 || rbase + RPP * i < KD)
             *reinterpret_cast<uint4 *>(Kt + (rbase + RPP * i) * LDKT + pk) = rk[i];
+#pragma unroll
+    for (int i = 0; i < V_PER; ++i) {
+        if (DV % RPP == 0 || rbase + RPP * i < DV) {  // V^T rows are 8-byte aligned
+            elem *dst = Vt + (rbase + RPP * i) * LDVT + pk;
+            reinterpret_cast<uint2 *>(dst)[0] = make_uint2(rv[i].x, rv[i].y);
+            reinterpret_cast<uint2 *>(dst)[1] = make_uint2(rv[i].z, rv[i].w);
+        }
+    }
     __syncthreads();
 
     // this wave: queries q0 + 32 qs + [0, 32), key blocks ks*NB + [0, NB)
@@ -390,38 +396,26 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int c = 0; c < 16; ++c) mx = fmaxf(mx, s[kb][c]);
         }
         m = xhalf_max(mx) * scale_log2;  // exact max of this half, log2 units
-        // a half with no keys keeps m = -inf and contributes nothing
+    }
+    if (active) {
+        // probabilities block by block, so that the exp2 of a block overlaps
+        // the P V products of the one before; the row sum is taken over the
+        // rounded probabilities the products use
+        // (a half with no keys keeps m = -inf and contributes nothing)
         const float neg_m = m == -INFINITY ? 0.f : -m;
 #pragma unroll
-        for (int kb = 0; kb < NB; ++kb)
+        for (int kb = 0; kb < NB; ++kb) {
 #pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][c], scale_log2, neg_m));
-                s[kb][c] = p;
-                l_run += p;
-            }
-    }
-    // V^T into LDS (its own region: K^T and Q^T may still be read); rows are
-    // 8-byte aligned
-#pragma unroll
-    for (int i = 0; i < V_PER; ++i) {
-        if (DV % RPP == 0 || rbase + RPP * i < DV) {
-            elem *dst = Vt + (rbase + RPP * i) * LDVT + pk;
-            reinterpret_cast<uint2 *>(dst)[0] = make_uint2(rv[i].x, rv[i].y);
-            reinterpret_cast<uint2 *>(dst)[1] = make_uint2(rv[i].z, rv[i].w);
-        }
-    }
-    __syncthreads();
-    if (active) {
-#pragma unroll
-        for (int kb = 0; kb < NB; ++kb)
+            for (int c = 0; c < 16; ++c) s[kb][c] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][c], scale_log2, neg_m));
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const frag pf = c_to_frag<DT>(s[kb], t);
+                l_run = Tr::sum_frag(pf, l_run);
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
                     acc[db] = Tr::mfma(ld_t_frag<DT>(Vt + (32 * db + col) * LDVT, kb0 + kb, t, h), pf, acc[db]);
             }
+        }
     }
     const float l_half = xhalf_sum(l_run);
     __syncthreads();  // K^T / V^T no longer read: reuse the space
