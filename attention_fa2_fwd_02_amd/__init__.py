@@ -11,10 +11,12 @@ GPU.
 
 Entry points (same names as the C ABI):
   fa2_fwd, fa2_bwd_delta, fa2_bwd_dq, fa2_bwd_dkdv, psa_pack_qkv, psa_merge_attn,
-  psa_attn_fused
+  psa_attn_fused, psa_merge_attn_backward, psa_pack_qkv_backward
 Compositions of them:
   attention_fwd (= fa2_fwd), attention_bwd (delta -> dkdv -> dq),
-  psa_block (pack -> fa2_fwd on V_lo -> fa2_fwd on V_hi -> merge)
+  psa_block (pack -> fa2_fwd on V_lo -> fa2_fwd on V_hi -> merge),
+  psa_block_backward (merge backward -> the attention backward of both calls
+  -> pack backward, adding the two calls' dQ and dK)
 """
 from __future__ import annotations
 
@@ -27,7 +29,8 @@ from ._lib import FA2_BF16, FA2_F16, FA2_F32, Fa2Error, library_path, load  # no
 
 __all__ = [
     "fa2_fwd", "fa2_bwd_delta", "fa2_bwd_dq", "fa2_bwd_dkdv", "psa_pack_qkv", "psa_merge_attn", "psa_attn_fused",
-    "attention_fwd", "attention_bwd", "psa_block", "Fa2Error", "load", "library_path",
+    "psa_merge_attn_backward", "psa_pack_qkv_backward",
+    "attention_fwd", "attention_bwd", "psa_block", "psa_block_backward", "Fa2Error", "load", "library_path",
 ]
 
 _DT = {torch.float32: FA2_F32, torch.float16: FA2_F16, torch.bfloat16: FA2_BF16}
@@ -217,3 +220,76 @@ def psa_attn_fused(qkv, num_heads: int, key_dim: int, out=None, lse=None):
     _lib.call("psa_attn_fused", _dtype_code(qkv), qkv.data_ptr(), out.data_ptr(), lse_ptr, b, num_heads, key_dim,
               h, w, _stream(qkv.device))
     return out
+
+
+def psa_merge_attn_backward(d_out, num_heads: int, key_dim: int, d_o_lo=None, d_o_hi=None):
+    """d_out [B, nh*2*kd, H, W] -> (d_o_lo, d_o_hi) [B*nh, H*W, kd]."""
+    _check("d_out", d_out)
+    b, ch, h, w = d_out.shape
+    if ch != num_heads * 2 * key_dim:
+        raise ValueError(f"d_out has {ch} channels, expected num_heads*2*key_dim = {num_heads * 2 * key_dim}")
+    shape = (b * num_heads, h * w, key_dim)
+    if d_o_lo is None:
+        d_o_lo = torch.empty(shape, dtype=d_out.dtype, device=d_out.device)
+    if d_o_hi is None:
+        d_o_hi = torch.empty(shape, dtype=d_out.dtype, device=d_out.device)
+    _check("d_o_lo", d_o_lo, d_out.dtype, shape, d_out.device)
+    _check("d_o_hi", d_o_hi, d_out.dtype, shape, d_out.device)
+    _lib.call("psa_merge_attn_backward", _dtype_code(d_out), d_out.data_ptr(), d_o_lo.data_ptr(), d_o_hi.data_ptr(),
+              b, num_heads, key_dim, h, w, _stream(d_out.device))
+    return d_o_lo, d_o_hi
+
+
+def psa_pack_qkv_backward(d_packed, batch: int, num_heads: int, h: int, w: int, d_qk_extra=None, d_qkv=None):
+    """d_packed [4, B*nh, H*W, kd] (+ d_qk_extra [2, B*nh, H*W, kd] added to the
+    dQ and dK sections) -> d_qkv [B, nh*4*kd, H, W]."""
+    _check("d_packed", d_packed)
+    if d_packed.dim() != 4 or d_packed.shape[0] != 4 or d_packed.shape[1] != batch * num_heads \
+            or d_packed.shape[2] != h * w:
+        raise ValueError(f"d_packed has shape {tuple(d_packed.shape)}, expected [4, batch*num_heads, h*w, key_dim]")
+    kd = d_packed.shape[3]
+    extra_ptr = None
+    if d_qk_extra is not None:
+        _check("d_qk_extra", d_qk_extra, d_packed.dtype, (2, batch * num_heads, h * w, kd), d_packed.device)
+        extra_ptr = d_qk_extra.data_ptr()
+    if d_qkv is None:
+        d_qkv = torch.empty((batch, num_heads * 4 * kd, h, w), dtype=d_packed.dtype, device=d_packed.device)
+    _check("d_qkv", d_qkv, d_packed.dtype, (batch, num_heads * 4 * kd, h, w), d_packed.device)
+    _lib.call("psa_pack_qkv_backward", _dtype_code(d_packed), d_packed.data_ptr(), extra_ptr, d_qkv.data_ptr(),
+              batch, num_heads, kd, h, w, _stream(d_packed.device))
+    return d_qkv
+
+
+def psa_block_backward(d_out, num_heads: int, key_dim: int, workspace: dict):
+    """Gradient of psa_block with respect to qkv. ``workspace`` is the dict of
+    the forward psa_block call on the same shapes (it holds the packed
+    operands, both attention outputs and the LSE); the backward's own buffers
+    are kept in it too. Steps: merge backward -> for V_lo and V_hi: delta,
+    dK/dV, dQ on the packed sections -> pack backward, which adds the second
+    call's dQ and dK to the first's. Returns d_qkv [B, nh*4*kd, H, W]."""
+    ws = workspace
+    _check("d_out", d_out)
+    b, ch, h, w = d_out.shape
+    key = ws.get("key")
+    if key is None or key[0][0] != b or key[0][2:] != (h, w) or key[1] != d_out.dtype or key[3:] != (num_heads, key_dim):
+        raise ValueError("workspace does not come from a psa_block forward on these shapes")
+    bh, n = b * num_heads, h * w
+    bkey = ("bwd",) + key
+    if ws.get("bwd_key") != bkey:
+        ws["bwd_key"] = bkey
+        ws["d_o"] = torch.empty((2, bh, n, key_dim), dtype=d_out.dtype, device=d_out.device)
+        ws["d_packed"] = torch.empty((4, bh, n, key_dim), dtype=d_out.dtype, device=d_out.device)
+        ws["d_qk_extra"] = torch.empty((2, bh, n, key_dim), dtype=d_out.dtype, device=d_out.device)
+        ws["delta"] = torch.empty((bh, n), dtype=torch.float32, device=d_out.device)
+        ws["d_qkv"] = torch.empty((b, num_heads * 4 * key_dim, h, w), dtype=d_out.dtype, device=d_out.device)
+    packed, o, lse = ws["packed"], ws["o"], ws["lse"]
+    d_o, d_packed, extra, delta = ws["d_o"], ws["d_packed"], ws["d_qk_extra"], ws["delta"]
+    psa_merge_attn_backward(d_out, num_heads, key_dim, d_o[0], d_o[1])
+    scale = 1.0 / math.sqrt(key_dim)
+    for half in (0, 1):
+        dq_dst, dk_dst = (d_packed[0], d_packed[1]) if half == 0 else (extra[0], extra[1])
+        fa2_bwd_delta(o[half], d_o[half], delta)
+        fa2_bwd_dkdv(packed[0], packed[1], packed[2 + half], d_o[half], lse, delta, scale, dk_dst, d_packed[2 + half])
+        fa2_bwd_dq(packed[0], packed[1], packed[2 + half], d_o[half], lse, delta, scale, dq_dst)
+    return psa_pack_qkv_backward(d_packed, b, num_heads, h, w, extra, ws["d_qkv"])
+

@@ -172,6 +172,32 @@ fa2_status psa_merge_attn(fa2_dtype dt, const void *o_lo, const void *o_hi, void
     return launched(fn, fa2mi::launch_psa_merge((int)dt, o_lo, o_hi, out, s, (hipStream_t)stream));
 }
 
+fa2_status psa_merge_attn_backward(fa2_dtype dt, const void *d_out, void *d_o_lo, void *d_o_hi, int32_t batch,
+                                   int32_t num_heads, int32_t key_dim, int32_t h, int32_t w, void *stream) {
+    static const char fn[] = "psa_merge_attn_backward";
+    fa2_status st = check_psa(fn, dt, batch, num_heads, key_dim, h, w);
+    if (st != FA2_OK) return st;
+    REQUIRE_PTR(fn, d_out);
+    REQUIRE_PTR(fn, d_o_lo);
+    REQUIRE_PTR(fn, d_o_hi);
+    const fa2mi::PsaShape s{batch, num_heads, key_dim, h * w};
+    return launched(fn, fa2mi::launch_psa_merge_backward((int)dt, d_out, d_o_lo, d_o_hi, s, (hipStream_t)stream));
+}
+
+fa2_status psa_pack_qkv_backward(fa2_dtype dt, const void *d_packed, const void *d_qk_extra, void *d_qkv,
+                                 int32_t batch, int32_t num_heads, int32_t key_dim, int32_t h, int32_t w,
+                                 void *stream) {
+    static const char fn[] = "psa_pack_qkv_backward";
+    fa2_status st = check_psa(fn, dt, batch, num_heads, key_dim, h, w);
+    if (st != FA2_OK) return st;
+    REQUIRE_PTR(fn, d_packed);
+    if (d_qk_extra != nullptr) REQUIRE_PTR(fn, d_qk_extra);
+    REQUIRE_PTR(fn, d_qkv);
+    const fa2mi::PsaShape s{batch, num_heads, key_dim, h * w};
+    return launched(fn, fa2mi::launch_psa_pack_backward((int)dt, d_packed, d_qk_extra, d_qkv, s,
+                                                         (hipStream_t)stream));
+}
+
 fa2_status psa_attn_fused(fa2_dtype dt, const void *qkv, void *out, float *lse, int32_t batch,
                           int32_t num_heads, int32_t key_dim, int32_t h, int32_t w, void *stream) {
     static const char fn[] = "psa_attn_fused";

@@ -38,6 +38,10 @@ hipError_t launch_psa_pack(int dt, const void *qkv, void *packed, const PsaShape
 hipError_t launch_psa_merge(int dt, const void *lo, const void *hi, void *out, const PsaShape &s,
                             hipStream_t stream);
 hipError_t launch_psa_fused(int dt, const void *qkv, void *out, float *lse, const PsaShape &s, hipStream_t stream);
+hipError_t launch_psa_merge_backward(int dt, const void *d_out, void *d_lo, void *d_hi, const PsaShape &s,
+                                     hipStream_t stream);
+hipError_t launch_psa_pack_backward(int dt, const void *d_packed, const void *d_qk_extra, void *d_qkv,
+                                    const PsaShape &s, hipStream_t stream);
 
 // Smallest query rows per forward / dq workgroup and key rows per dkdv
 // workgroup (the ABI checks that the 1-D grids fit in int32).

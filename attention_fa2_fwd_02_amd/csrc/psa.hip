@@ -1,5 +1,6 @@
 // PSA rearrangements around the attention of a C2PSA block (vision_rs
-// psa.rs, "psa_pack_qkv" and "psa_merge_attn_nchw"). Both are batched
+// psa.rs, "psa_pack_qkv", "psa_merge_attn_nchw" and their backward kernels
+// "psa_pack_qkv_backward", "psa_merge_attn_backward"). All are batched
 // transposes between a channel-major NCHW slice [kd channels][hw pixels] and
 // a pixel-major attention operand [hw rows][kd]:
 //   pack : slice (b, head, s) of qkv = channels head*4kd + s*kd .. +kd of
@@ -8,7 +9,10 @@
 //          [hw][kd] block (s*BH + b*nh + head)*hw*kd;
 //   merge: o_lo / o_hi head bh ([hw][kd] at bh*hw*kd) go to out channels
 //          head*2kd (+kd for hi) of batch b: the contiguous [kd][hw] block
-//          (2*bh + half)*kd*hw.
+//          (2*bh + half)*kd*hw;
+//   merge backward: the inverse of merge (d_out slices to d_o_lo / d_o_hi);
+//   pack backward : the inverse of pack (d_packed sections to d_qkv slices),
+//          optionally adding a second Q/K gradient pair.
 // One workgroup moves a kd x P tile (P pixels) through LDS so that global
 // reads and writes are both contiguous 16-byte vectors.
 #include "fa2_device.h"
@@ -44,22 +48,31 @@ __device__ __forceinline__ void st_vec(elem *dst, const uint4 &v, int avail) {
     }
 }
 
-// [KD][hw] slice -> [hw][KD] slice, tile of P pixels per workgroup.
+// Up to four section pointers, passed by value.
+struct SecPtrs {
+    const void *p[4];
+};
+
+// [KD][hw] channel slices -> [hw][KD] row slices, tile of P pixels per
+// workgroup. Source slice `slice` (the contiguous [KD][hw] block `slice` of
+// src) is (head row bhh, section s) with slice = bhh * NSEC + s; it goes to
+// dst[s] + bhh * hw * KD. pack: NSEC = 4 (Q, K, V_lo, V_hi sections of the
+// packed buffer); merge backward: NSEC = 2 (d_o_lo, d_o_hi).
 // ALIGNED: hw is a multiple of VEC, so pixel vectors never straddle a row end.
-template <typename elem, int KD, bool ALIGNED>
-__global__ __launch_bounds__(256) void pack_kernel(const elem *__restrict__ qkv, elem *__restrict__ packed,
-                                                   int nh, int bh, int hw, int tiles_per_slice) {
+template <typename elem, int KD, int NSEC, bool ALIGNED>
+__global__ __launch_bounds__(256) void to_rows_kernel(const elem *__restrict__ src_all, SecPtrs dst_sec, int hw,
+                                                      int tiles_per_slice) {
     constexpr int VEC = 16 / (int)sizeof(elem);
     constexpr int P = 256 * VEC / KD;  // pixels per tile
     constexpr int LD = P + VEC;        // LDS row stride (channel rows)
     __shared__ __attribute__((aligned(16))) elem tile[KD * LD];
 
     const int tid = threadIdx.x;
-    const int slice = blockIdx.x / tiles_per_slice;  // (b*nh + head)*4 + s
+    const int slice = blockIdx.x / tiles_per_slice;
     const int p0 = (blockIdx.x % tiles_per_slice) * P;
-    const int s = slice % 4, bhh = slice / 4;
-    const elem *src = qkv + (int64_t)slice * KD * hw;
-    elem *dst = packed + ((int64_t)s * bh + bhh) * hw * KD;
+    const int s = slice % NSEC, bhh = slice / NSEC;
+    const elem *src = src_all + (int64_t)slice * KD * hw;
+    elem *dst = const_cast<elem *>(static_cast<const elem *>(dst_sec.p[s])) + (int64_t)bhh * hw * KD;
 
     {   // read: channel row c, pixel vector pv
         const int c = tid / (P / VEC), pv = tid % (P / VEC);
@@ -79,29 +92,49 @@ __global__ __launch_bounds__(256) void pack_kernel(const elem *__restrict__ qkv,
             *reinterpret_cast<uint4 *>(dst + (int64_t)(p0 + p) * KD + cv * VEC) = v;
         }
     }
-    (void)nh;
 }
 
-// [hw][KD] slice -> [KD][hw] slice.
-template <typename elem, int KD, bool ALIGNED>
-__global__ __launch_bounds__(256) void merge_kernel(const elem *__restrict__ lo, const elem *__restrict__ hi,
-                                                    elem *__restrict__ out, int hw, int tiles_per_slice) {
+// [hw][KD] row slices -> [KD][hw] channel slices. Destination slice
+// slice = bhh * NSEC + s (the contiguous [KD][hw] block `slice` of out) is
+// read from src[s] + bhh * hw * KD. merge: NSEC = 2 (o_lo, o_hi); pack
+// backward: NSEC = 4 (the sections of d_packed). ADD: sections 0 and 1 also
+// add add_sec[s] + bhh * hw * KD (the second V-split call's dQ and dK) in
+// fp32 before rounding; T is then the element type, else any type of the
+// element's size (the copy moves bits).
+template <typename T, int KD, int NSEC, bool ADD, bool ALIGNED>
+__global__ __launch_bounds__(256) void to_channels_kernel(SecPtrs src_sec, SecPtrs add_sec, T *__restrict__ out,
+                                                          int hw, int tiles_per_slice) {
+    using elem = T;
     constexpr int VEC = 16 / (int)sizeof(elem);
     constexpr int P = 256 * VEC / KD;
     constexpr int LD = KD + VEC;  // LDS row stride (pixel rows)
     __shared__ __attribute__((aligned(16))) elem tile[P * LD];
 
     const int tid = threadIdx.x;
-    const int slice = blockIdx.x / tiles_per_slice;  // 2*bh + half
+    const int slice = blockIdx.x / tiles_per_slice;
     const int p0 = (blockIdx.x % tiles_per_slice) * P;
-    const int half = slice & 1, bhh = slice >> 1;
-    const elem *src = (half ? hi : lo) + (int64_t)bhh * hw * KD;
+    const int s = slice % NSEC, bhh = slice / NSEC;
+    const elem *src = static_cast<const elem *>(src_sec.p[s]) + (int64_t)bhh * hw * KD;
     elem *dst = out + (int64_t)slice * KD * hw;
 
     {   // read: pixel p, channel vector cv (contiguous P x KD block)
         const int p = tid / (KD / VEC), cv = tid % (KD / VEC);
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (p0 + p < hw) v = *reinterpret_cast<const uint4 *>(src + (int64_t)(p0 + p) * KD + cv * VEC);
+        if (p0 + p < hw) {
+            const int64_t off = (int64_t)(p0 + p) * KD + cv * VEC;
+            v = *reinterpret_cast<const uint4 *>(src + off);
+            if constexpr (ADD) {
+                if (s < 2) {
+                    const uint4 w = *reinterpret_cast<const uint4 *>(static_cast<const elem *>(add_sec.p[s]) +
+                                                                     (int64_t)bhh * hw * KD + off);
+                    elem *ev = reinterpret_cast<elem *>(&v);
+                    const elem *ew = reinterpret_cast<const elem *>(&w);
+#pragma unroll
+                    for (int i = 0; i < VEC; ++i)
+                        ev[i] = static_cast<elem>(static_cast<float>(ev[i]) + static_cast<float>(ew[i]));
+                }
+            }
+        }
         *reinterpret_cast<uint4 *>(tile + p * LD + cv * VEC) = v;
     }
     __syncthreads();
@@ -118,66 +151,101 @@ __global__ __launch_bounds__(256) void merge_kernel(const elem *__restrict__ lo,
     }
 }
 
-template <typename elem, int KD>
-static hipError_t pack_dispatch(const void *qkv, void *packed, const PsaShape &s, hipStream_t stream) {
+template <typename elem, int KD, int NSEC>
+static hipError_t to_rows_dispatch(const void *src, const SecPtrs &dst, const PsaShape &s, hipStream_t stream) {
     constexpr int VEC = 16 / (int)sizeof(elem);
     constexpr int P = 256 * VEC / KD;
     const int tps = (s.hw + P - 1) / P;
-    const int bh = s.batch * s.num_heads;
-    const int grid = bh * 4 * tps;
+    const int grid = s.batch * s.num_heads * NSEC * tps;
     if (s.hw % VEC == 0)
-        hipLaunchKernelGGL((pack_kernel<elem, KD, true>), dim3(grid), dim3(256), 0, stream, (const elem *)qkv,
-                           (elem *)packed, s.num_heads, bh, s.hw, tps);
+        hipLaunchKernelGGL((to_rows_kernel<elem, KD, NSEC, true>), dim3(grid), dim3(256), 0, stream,
+                           (const elem *)src, dst, s.hw, tps);
     else
-        hipLaunchKernelGGL((pack_kernel<elem, KD, false>), dim3(grid), dim3(256), 0, stream, (const elem *)qkv,
-                           (elem *)packed, s.num_heads, bh, s.hw, tps);
+        hipLaunchKernelGGL((to_rows_kernel<elem, KD, NSEC, false>), dim3(grid), dim3(256), 0, stream,
+                           (const elem *)src, dst, s.hw, tps);
     return hipGetLastError();
 }
 
-template <typename elem, int KD>
-static hipError_t merge_dispatch(const void *lo, const void *hi, void *out, const PsaShape &s, hipStream_t stream) {
-    constexpr int VEC = 16 / (int)sizeof(elem);
+template <typename T, int KD, int NSEC, bool ADD>
+static hipError_t to_channels_dispatch(const SecPtrs &src, const SecPtrs &add, void *out, const PsaShape &s,
+                                       hipStream_t stream) {
+    constexpr int VEC = 16 / (int)sizeof(T);
     constexpr int P = 256 * VEC / KD;
     const int tps = (s.hw + P - 1) / P;
-    const int bh = s.batch * s.num_heads;
-    const int grid = bh * 2 * tps;
+    const int grid = s.batch * s.num_heads * NSEC * tps;
     if (s.hw % VEC == 0)
-        hipLaunchKernelGGL((merge_kernel<elem, KD, true>), dim3(grid), dim3(256), 0, stream, (const elem *)lo,
-                           (const elem *)hi, (elem *)out, s.hw, tps);
+        hipLaunchKernelGGL((to_channels_kernel<T, KD, NSEC, ADD, true>), dim3(grid), dim3(256), 0, stream, src, add,
+                           (T *)out, s.hw, tps);
     else
-        hipLaunchKernelGGL((merge_kernel<elem, KD, false>), dim3(grid), dim3(256), 0, stream, (const elem *)lo,
-                           (const elem *)hi, (elem *)out, s.hw, tps);
+        hipLaunchKernelGGL((to_channels_kernel<T, KD, NSEC, ADD, false>), dim3(grid), dim3(256), 0, stream, src,
+                           add, (T *)out, s.hw, tps);
     return hipGetLastError();
 }
 
-// The rearrangements copy bits, so only the element size matters.
-template <typename elem>
-static hipError_t pack_by_kd(const void *qkv, void *packed, const PsaShape &s, hipStream_t st) {
+template <typename elem, int NSEC>
+static hipError_t to_rows_by_kd(const void *src, const SecPtrs &dst, const PsaShape &s, hipStream_t st) {
     switch (s.key_dim) {
-        case 32: return pack_dispatch<elem, 32>(qkv, packed, s, st);
-        case 64: return pack_dispatch<elem, 64>(qkv, packed, s, st);
-        case 128: return pack_dispatch<elem, 128>(qkv, packed, s, st);
+        case 32: return to_rows_dispatch<elem, 32, NSEC>(src, dst, s, st);
+        case 64: return to_rows_dispatch<elem, 64, NSEC>(src, dst, s, st);
+        case 128: return to_rows_dispatch<elem, 128, NSEC>(src, dst, s, st);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <typename elem>
-static hipError_t merge_by_kd(const void *lo, const void *hi, void *out, const PsaShape &s, hipStream_t st) {
+template <typename T, int NSEC, bool ADD>
+static hipError_t to_channels_by_kd(const SecPtrs &src, const SecPtrs &add, void *out, const PsaShape &s,
+                                    hipStream_t st) {
     switch (s.key_dim) {
-        case 32: return merge_dispatch<elem, 32>(lo, hi, out, s, st);
-        case 64: return merge_dispatch<elem, 64>(lo, hi, out, s, st);
-        case 128: return merge_dispatch<elem, 128>(lo, hi, out, s, st);
+        case 32: return to_channels_dispatch<T, 32, NSEC, ADD>(src, add, out, s, st);
+        case 64: return to_channels_dispatch<T, 64, NSEC, ADD>(src, add, out, s, st);
+        case 128: return to_channels_dispatch<T, 128, NSEC, ADD>(src, add, out, s, st);
         default: return hipErrorInvalidValue;
     }
+}
+
+// Section pointers of a section-major buffer [n][B*nh][hw][kd].
+static SecPtrs sections(const void *base, int n, const PsaShape &s, int esize) {
+    SecPtrs r{};
+    const int64_t sec_bytes = (int64_t)s.batch * s.num_heads * s.hw * s.key_dim * esize;
+    for (int i = 0; i < n; ++i) r.p[i] = static_cast<const char *>(base) + i * sec_bytes;
+    return r;
 }
 
 hipError_t launch_psa_pack(int dt, const void *qkv, void *packed, const PsaShape &s, hipStream_t stream) {
-    return dt == 0 ? pack_by_kd<uint32_t>(qkv, packed, s, stream) : pack_by_kd<uint16_t>(qkv, packed, s, stream);
+    if (dt == 0) return to_rows_by_kd<uint32_t, 4>(qkv, sections(packed, 4, s, 4), s, stream);
+    return to_rows_by_kd<uint16_t, 4>(qkv, sections(packed, 4, s, 2), s, stream);
 }
 
 hipError_t launch_psa_merge(int dt, const void *lo, const void *hi, void *out, const PsaShape &s,
                             hipStream_t stream) {
-    return dt == 0 ? merge_by_kd<uint32_t>(lo, hi, out, s, stream) : merge_by_kd<uint16_t>(lo, hi, out, s, stream);
+    const SecPtrs src{{lo, hi, nullptr, nullptr}}, none{};
+    if (dt == 0) return to_channels_by_kd<uint32_t, 2, false>(src, none, out, s, stream);
+    return to_channels_by_kd<uint16_t, 2, false>(src, none, out, s, stream);
+}
+
+hipError_t launch_psa_merge_backward(int dt, const void *d_out, void *d_lo, void *d_hi, const PsaShape &s,
+                                     hipStream_t stream) {
+    const SecPtrs dst{{d_lo, d_hi, nullptr, nullptr}};
+    if (dt == 0) return to_rows_by_kd<uint32_t, 2>(d_out, dst, s, stream);
+    return to_rows_by_kd<uint16_t, 2>(d_out, dst, s, stream);
+}
+
+hipError_t launch_psa_pack_backward(int dt, const void *d_packed, const void *d_qk_extra, void *d_qkv,
+                                    const PsaShape &s, hipStream_t stream) {
+    const int es = dt == 0 ? 4 : 2;
+    const SecPtrs src = sections(d_packed, 4, s, es);
+    if (d_qk_extra == nullptr) {
+        const SecPtrs none{};
+        if (dt == 0) return to_channels_by_kd<uint32_t, 4, false>(src, none, d_qkv, s, stream);
+        return to_channels_by_kd<uint16_t, 4, false>(src, none, d_qkv, s, stream);
+    }
+    const SecPtrs add = sections(d_qk_extra, 2, s, es);
+    switch (dt) {
+        case 0: return to_channels_by_kd<float, 4, true>(src, add, d_qkv, s, stream);
+        case 1: return to_channels_by_kd<_Float16, 4, true>(src, add, d_qkv, s, stream);
+        case 2: return to_channels_by_kd<__bf16, 4, true>(src, add, d_qkv, s, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace fa2mi

@@ -383,6 +383,14 @@ def _leg_c2(torch, fa2, workloads, dev, legs):
     fused_bytes = byts["fused"]  # qkv read once, out written once
     fused_stream = _time_batch(torch, lambda: fa2.psa_attn_fused(qkv, w2.num_heads, w2.key_dim, out_f), 200)
     block_stream = _time_batch(torch, lambda: fa2.psa_block(qkv, w2.num_heads, w2.key_dim, ws), 200)
+    # backward of the block (merge backward, attention backward of both
+    # calls, pack backward) from the forward's workspace
+    fa2.psa_block(qkv, w2.num_heads, w2.key_dim, ws)
+    g = torch.Generator(device=dev)
+    g.manual_seed(w2.seed + 1000)
+    d_out = torch.randn((w2.batch, w2.out_channels, w2.h, w2.w), generator=g, device=dev).to(w2.torch_dtype)
+    bwd_warm = _time_fn(torch, lambda: fa2.psa_block_backward(d_out, w2.num_heads, w2.key_dim, ws), 50)
+    bwd_stream = _time_batch(torch, lambda: fa2.psa_block_backward(d_out, w2.num_heads, w2.key_dim, ws), 200)
     legs["c2"] = {
         "fused_us_per_call_stream": round(fused_stream * 1e3, 2),
         "block_us_per_call_stream": round(block_stream * 1e3, 2),
@@ -397,6 +405,8 @@ def _leg_c2(torch, fa2, workloads, dev, legs):
         "gbs_cold": round(total_bytes / (cold * 1e-3) / 1e9, 1),
         "frac_hbm_cold": round(total_bytes / (cold * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "attn_tflops_warm": round(w2.attn_flops() / (warm * 1e-3) / 1e12, 2),
+        "bwd_us_per_call_warm": round(bwd_warm * 1e3, 2),
+        "bwd_us_per_call_stream": round(bwd_stream * 1e3, 2),
     }
     print(f"[bench] leg c2 {legs['c2']}", file=sys.stderr, flush=True)
 

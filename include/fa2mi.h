@@ -156,6 +156,41 @@ fa2_status psa_attn_fused(fa2_dtype dt, const void *qkv, void *out, float *lse,
                           int32_t batch, int32_t num_heads, int32_t key_dim, int32_t h, int32_t w,
                           void *stream);
 
+/*
+ * Backward of psa_merge_attn (vision_rs psa.rs, "psa_merge_attn_backward"):
+ * d_out is the gradient of the merged NCHW output, [batch,
+ * num_heads*2*key_dim, h, w]; writes the gradients of the two attention
+ * outputs, [batch*num_heads, h*w, key_dim] each:
+ *   d_o_lo[b*num_heads + hd][n][d] = d_out[b][hd*2*key_dim + d][n]
+ *   d_o_hi[b*num_heads + hd][n][d] = d_out[b][hd*2*key_dim + key_dim + d][n].
+ * Bit-exact copy (the inverse permutation of psa_merge_attn); every element
+ * of d_o_lo and d_o_hi is written. dt is F16, BF16 or F32.
+ */
+fa2_status psa_merge_attn_backward(fa2_dtype dt, const void *d_out, void *d_o_lo, void *d_o_hi,
+                                   int32_t batch, int32_t num_heads, int32_t key_dim, int32_t h, int32_t w,
+                                   void *stream);
+
+/*
+ * Backward of psa_pack_qkv (vision_rs psa.rs, "psa_pack_qkv_backward"):
+ * d_packed is the gradient of the packed buffer, [4, batch*num_heads, h*w,
+ * key_dim] (sections dQ, dK, dV_lo, dV_hi); writes the NCHW gradient of the
+ * qkv activation [batch, num_heads*4*key_dim, h, w]:
+ *   d_qkv[b][hd*4*key_dim + s*key_dim + d][n] = d_packed[s][b*num_heads + hd][n][d]
+ *                                               (+ d_qk_extra[s][...][n][d] for s < 2).
+ * d_qk_extra, if not NULL, is a second [2, batch*num_heads, h*w, key_dim]
+ * pair (dQ, dK) added to sections 0 and 1: the V-split block runs attention
+ * twice on the same Q and K, and the page's combined backward adds both
+ * calls' dQ and dK atomically; here the second call's pair is passed
+ * separately and added in fp32 before rounding. Without it the result is a
+ * bit-exact copy (the inverse permutation of psa_pack_qkv). d_qkv is
+ * overwritten entirely (the page accumulates with atomics because a second
+ * kernel also adds into the V channels; no such kernel is part of this
+ * library). dt is F16, BF16 or F32.
+ */
+fa2_status psa_pack_qkv_backward(fa2_dtype dt, const void *d_packed, const void *d_qk_extra, void *d_qkv,
+                                 int32_t batch, int32_t num_heads, int32_t key_dim, int32_t h, int32_t w,
+                                 void *stream);
+
 #ifdef __cplusplus
 }
 #endif

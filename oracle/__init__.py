@@ -18,6 +18,12 @@ What each routine follows:
   * ``psa_block`` - pack, attention on (Q, K, V_lo) and (Q, K, V_hi) at
     scale 1/sqrt(key_dim), merge (psa.rs module doc, the V-split trick, and
     "FlashAttn2PsaRuntimeOp").
+  * ``psa_merge_backward`` / ``psa_pack_backward`` - the inverse index maps
+    (psa.rs "psa_merge_attn_backward", "psa_pack_qkv_backward").
+  * ``psa_block_backward`` - the block's gradient by the chain rule in the
+    order of psa.rs's backward: merge backward, the attention gradients of
+    both calls (dQ and dK summed over the two calls, as that page's combined
+    backward adds them), pack backward.
 
 Every routine is pinned by the CPU tests in tests/test_oracle_*.py against
 values and facts that do not come from this code (hand-worked cases, a page's
@@ -70,6 +76,8 @@ def _load():
         lib.oracle_psa_pack.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int] + [_i64] * 4
         lib.oracle_psa_merge.restype = ctypes.c_int
         lib.oracle_psa_merge.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] + [_i64] * 4
+        lib.oracle_psa_merge_backward.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] + [_i64] * 4
+        lib.oracle_psa_pack_backward.argtypes = [ctypes.c_void_p] * 2 + [ctypes.c_int] + [_i64] * 4
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -187,6 +195,49 @@ def psa_block(qkv, num_heads: int, key_dim: int, threads: int | None = None) -> 
     o_lo, _ = attention_fwd(packed[0], packed[1], packed[2], scale, threads)
     o_hi, _ = attention_fwd(packed[0], packed[1], packed[3], scale, threads)
     return psa_merge(o_lo, o_hi, b, num_heads, key_dim, h, w)
+
+
+def psa_merge_backward(d_out, num_heads: int, key_dim: int):
+    """d_out [B, nh*2*kd, H, W] -> (d_lo, d_hi) [B*nh, H*W, kd], bit-exact copy."""
+    src = _raw(d_out)
+    b, ch, h, w = src.shape
+    if ch != num_heads * 2 * key_dim:
+        raise ValueError("channel count is not num_heads*2*key_dim")
+    lo = np.empty((b * num_heads, h * w, key_dim), src.dtype)
+    hi = np.empty_like(lo)
+    rc = _load().oracle_psa_merge_backward(src.ctypes.data, lo.ctypes.data, hi.ctypes.data, src.itemsize,
+                                           b, num_heads, key_dim, h * w)
+    if rc != 0:
+        raise RuntimeError("oracle_psa_merge_backward failed")
+    return lo, hi
+
+
+def psa_pack_backward(d_packed, batch: int, num_heads: int, h: int, w: int) -> np.ndarray:
+    """d_packed [4, B*nh, H*W, kd] -> d_qkv [B, nh*4*kd, H, W], bit-exact copy."""
+    src = _raw(d_packed)
+    if src.ndim != 4 or src.shape[0] != 4 or src.shape[1] != batch * num_heads or src.shape[2] != h * w:
+        raise ValueError("d_packed shape mismatch")
+    kd = src.shape[3]
+    out = np.empty((batch, num_heads * 4 * kd, h, w), src.dtype)
+    rc = _load().oracle_psa_pack_backward(src.ctypes.data, out.ctypes.data, src.itemsize,
+                                          batch, num_heads, kd, h * w)
+    if rc != 0:
+        raise RuntimeError("oracle_psa_pack_backward failed")
+    return out
+
+
+def psa_block_backward(qkv, num_heads: int, key_dim: int, d_out, threads: int | None = None) -> np.ndarray:
+    """Gradient of sum(psa_block(qkv) * d_out) with respect to qkv, fp64.
+    Returns d_qkv [B, nh*4*kd, H, W]."""
+    x, g = _f64(qkv), _f64(d_out)
+    b, _, h, w = x.shape
+    packed = psa_pack(x, num_heads, key_dim)
+    d_lo, d_hi = psa_merge_backward(g, num_heads, key_dim)
+    scale = 1.0 / np.sqrt(key_dim)
+    dq_lo, dk_lo, dv_lo = attention_bwd(packed[0], packed[1], packed[2], d_lo, scale, threads)
+    dq_hi, dk_hi, dv_hi = attention_bwd(packed[0], packed[1], packed[3], d_hi, scale, threads)
+    d_packed = np.stack([dq_lo + dq_hi, dk_lo + dk_hi, dv_lo, dv_hi])
+    return psa_pack_backward(d_packed, b, num_heads, h, w)
 
 
 if __name__ == "__main__":  # pragma: no cover

@@ -23,7 +23,9 @@
  *   dV_j  = sum_i P_ij dO_i
  *
  * PSA rearrangements (vision_rs psa.rs, "psa_pack_qkv" and
- * "psa_merge_attn_nchw"): pure index maps, copied element by element.
+ * "psa_merge_attn_nchw", and their backward kernels "psa_pack_qkv_backward"
+ * and "psa_merge_attn_backward"): pure index maps, copied element by element.
+ * The gradient of a permutation is the inverse permutation of the gradient.
  *
  * The query/key head dim (d) and the value head dim (dv) are separate so that
  * one attention with dv = 2*key_dim can be compared with two at dv = key_dim.
@@ -212,5 +214,49 @@ int oracle_psa_merge(const void *lo, const void *hi, void *out, int esize,
                     memcpy(dst + d_lo * esize, a + so * esize, (size_t)esize);
                     memcpy(dst + d_hi * esize, bsrc + so * esize, (size_t)esize);
                 }
+    return 0;
+}
+
+/* psa_merge_attn_backward: d_out NCHW [B, nh*2*kd, H*W] -> d_lo, d_hi
+ * [B*nh, H*W, kd], the inverse of psa_merge_attn_nchw:
+ *   d_lo[b*nh+h][n][d] = d_out[b][h*2*kd + d][n]
+ *   d_hi[b*nh+h][n][d] = d_out[b][h*2*kd + kd + d][n] */
+int oracle_psa_merge_backward(const void *d_out, void *d_lo, void *d_hi, int esize,
+                              int64_t batch, int64_t nh, int64_t kd, int64_t hw) {
+    if (batch <= 0 || nh <= 0 || kd <= 0 || hw <= 0 || esize <= 0) return -1;
+    const char *src = (const char *)d_out;
+    char *lo = (char *)d_lo, *hi = (char *)d_hi;
+    int64_t c = nh * 2 * kd;
+    for (int64_t b = 0; b < batch; ++b)
+        for (int64_t h = 0; h < nh; ++h)
+            for (int64_t n = 0; n < hw; ++n)
+                for (int64_t d = 0; d < kd; ++d) {
+                    int64_t dof = ((b * nh + h) * hw + n) * kd + d;
+                    int64_t s_lo = (b * c + h * 2 * kd + d) * hw + n;
+                    int64_t s_hi = (b * c + h * 2 * kd + kd + d) * hw + n;
+                    memcpy(lo + dof * esize, src + s_lo * esize, (size_t)esize);
+                    memcpy(hi + dof * esize, src + s_hi * esize, (size_t)esize);
+                }
+    return 0;
+}
+
+/* psa_pack_qkv_backward: d_packed [4, B*nh, H*W, kd] -> d_qkv NCHW
+ * [B, nh*4*kd, H*W], the inverse of psa_pack_qkv:
+ *   d_qkv[b][h*4*kd + s*kd + d][n] = d_packed[s][b*nh+h][n][d] */
+int oracle_psa_pack_backward(const void *d_packed, void *d_qkv, int esize,
+                             int64_t batch, int64_t nh, int64_t kd, int64_t hw) {
+    if (batch <= 0 || nh <= 0 || kd <= 0 || hw <= 0 || esize <= 0) return -1;
+    const char *src = (const char *)d_packed;
+    char *dst = (char *)d_qkv;
+    int64_t bh = batch * nh, qkv_ch = nh * 4 * kd;
+    for (int64_t s = 0; s < 4; ++s)
+        for (int64_t b = 0; b < batch; ++b)
+            for (int64_t h = 0; h < nh; ++h)
+                for (int64_t n = 0; n < hw; ++n)
+                    for (int64_t d = 0; d < kd; ++d) {
+                        int64_t so = ((s * bh + b * nh + h) * hw + n) * kd + d;
+                        int64_t dof = (b * qkv_ch + h * 4 * kd + s * kd + d) * hw + n;
+                        memcpy(dst + dof * esize, src + so * esize, (size_t)esize);
+                    }
     return 0;
 }

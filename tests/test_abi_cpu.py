@@ -85,6 +85,14 @@ def test_bwd_and_psa_reject_invalid_arguments():
     assert lib.psa_attn_fused(1, A, None, None, 16, 4, 32, 20, 20, None) == INVALID
     assert lib.psa_attn_fused(2, A, A, A + 2, 16, 4, 32, 20, 20, None) == INVALID     # lse misaligned
     assert lib.psa_attn_fused(2, A, A, A, 16, 4, 32, 0, 20, None) == INVALID
+    assert lib.psa_merge_attn_backward(1, A, A, None, 16, 4, 32, 20, 20, None) == INVALID
+    assert lib.psa_merge_attn_backward(1, A, A, A, 16, 4, 48, 20, 20, None) == UNSUPPORTED
+    assert lib.psa_merge_attn_backward(1, A, MIS, A, 16, 4, 32, 20, 20, None) == INVALID
+    assert b"psa_merge_attn_backward" in lib.fa2_last_error()
+    assert lib.psa_pack_qkv_backward(2, None, None, A, 16, 4, 32, 20, 20, None) == INVALID
+    assert lib.psa_pack_qkv_backward(2, A, MIS, A, 16, 4, 32, 20, 20, None) == INVALID    # extra misaligned
+    assert lib.psa_pack_qkv_backward(2, A, None, A, 0, 4, 32, 20, 20, None) == INVALID
+    assert lib.psa_pack_qkv_backward(9, A, None, A, 16, 4, 32, 20, 20, None) == INVALID
 
 
 def test_binding_refuses_host_tensors():

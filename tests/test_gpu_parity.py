@@ -301,3 +301,84 @@ def test_psa_attn_fused_no_lse_and_canary():
     fa2.psa_attn_fused(qkv, wl.num_heads, wl.key_dim, out=out)
     torch.cuda.synchronize()
     assert torch.isnan(buf[n:]).all() and torch.isfinite(out).all()
+
+
+# ---------------------------------------------------------------------------
+# PSA backward: merge backward, pack backward, the composed block gradient
+
+
+def _bitsof(t, dt):
+    return t.cpu().view(torch.int32 if dt == "f32" else torch.int16).numpy()
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("kd,b,nh,h,w", [(32, 16, 4, 20, 20), (32, 2, 3, 5, 7), (64, 1, 2, 9, 9),
+                                         (128, 2, 1, 4, 6), (32, 1, 1, 1, 1)])
+def test_psa_merge_pack_backward_bitexact(dt, kd, b, nh, h, w):
+    dtype = DTYPES[dt]
+    case = f"psa bwd maps {dt} kd={kd} b={b} nh={nh} h={h} w={w}"
+    print(case, flush=True)
+    g = torch.Generator(device="cpu").manual_seed(31 + kd + h * w)
+    d_out = torch.randn(b, nh * 2 * kd, h, w, generator=g).to(DEV, dtype)
+    d_packed = torch.randn(4, b * nh, h * w, kd, generator=g).to(DEV, dtype)
+    lo, hi = fa2.psa_merge_attn_backward(d_out, nh, kd)
+    d_qkv = fa2.psa_pack_qkv_backward(d_packed, b, nh, h, w)
+    torch.cuda.synchronize()
+    bits = (lambda a: a.view(np.int32)) if dt == "f32" else (lambda a: a.view(np.int16))
+    want_lo, want_hi = oracle.psa_merge_backward(d_out, nh, kd)
+    assert np.array_equal(_bitsof(lo, dt), bits(want_lo)) and np.array_equal(_bitsof(hi, dt), bits(want_hi))
+    assert np.array_equal(_bitsof(d_qkv, dt), bits(oracle.psa_pack_backward(d_packed, b, nh, h, w)))
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("kd,b,nh,h,w", [(32, 2, 3, 5, 7), (64, 1, 2, 9, 9), (32, 16, 4, 20, 20)])
+def test_psa_pack_backward_adds_second_qk(dt, kd, b, nh, h, w):
+    """With d_qk_extra, sections 0 and 1 are the sum (in fp32, one rounding)
+    of the two Q/K gradients; V sections stay a bit-exact copy."""
+    dtype = DTYPES[dt]
+    case = f"psa pack bwd + extra {dt} kd={kd} b={b} nh={nh} h={h} w={w}"
+    print(case, flush=True)
+    g = torch.Generator(device="cpu").manual_seed(41 + kd + h * w)
+    d_packed = torch.randn(4, b * nh, h * w, kd, generator=g).to(DEV, dtype)
+    extra = torch.randn(2, b * nh, h * w, kd, generator=g).to(DEV, dtype)
+    got = fa2.psa_pack_qkv_backward(d_packed, b, nh, h, w, d_qk_extra=extra)
+    torch.cuda.synchronize()
+    summed = _np(d_packed).copy()
+    summed[:2] += _np(extra)
+    want = oracle.psa_pack_backward(summed, b, nh, h, w)
+    # one rounding of the exact sum to the element type: at most half an ulp
+    ulp = {torch.float32: 2.0 ** -23, torch.float16: 2.0 ** -10, torch.bfloat16: 2.0 ** -7}[dtype]
+    bound = ulp * np.maximum(np.abs(want), 2.0 ** -14)
+    assert np.all(np.abs(_np(got) - want) <= bound), case
+    v_sec = _np(got).reshape(b, nh, 4, kd, h * w)[:, :, 2:]
+    v_want = want.reshape(b, nh, 4, kd, h * w)[:, :, 2:]
+    assert np.array_equal(v_sec, v_want)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("kd,b,nh,h,w", [(32, 16, 4, 20, 20), (32, 2, 3, 5, 7), (64, 1, 2, 9, 9),
+                                         (32, 1, 2, 13, 11)])
+def test_psa_block_backward(dt, kd, b, nh, h, w):
+    dtype = DTYPES[dt]
+    case = f"psa block bwd {dt} kd={kd} b={b} nh={nh} h={h} w={w}"
+    print(case, flush=True)
+    wl = workloads.PsaWorkload("case", b, nh, kd, h, w, dt, seed=51 + kd + h * w)
+    qkv = workloads.psa_inputs(wl, device=DEV)
+    g = torch.Generator(device="cpu").manual_seed(52 + kd + h * w)
+    d_out = torch.randn(b, nh * 2 * kd, h, w, generator=g).to(DEV, dtype)
+    ws = {}
+    fa2.psa_block(qkv, nh, kd, ws)
+    d_qkv = fa2.psa_block_backward(d_out, nh, kd, ws)
+    torch.cuda.synchronize()
+    want = oracle.psa_block_backward(qkv, nh, kd, d_out)
+    _err("d_qkv", _np(d_qkv), want, TOL[dtype], case)
+    # the workspace is reused on a second call with the same shapes: same bits
+    first = d_qkv.clone()
+    d_qkv2 = fa2.psa_block_backward(d_out, nh, kd, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(first, d_qkv2)
+
+
+def test_psa_block_backward_needs_forward_workspace():
+    with pytest.raises(ValueError, match="workspace"):
+        fa2.psa_block_backward(torch.zeros(1, 64, 2, 2, dtype=torch.float16, device=DEV), 1, 32, {})

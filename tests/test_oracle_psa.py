@@ -1,7 +1,9 @@
-"""Pins for the oracle's PSA rearrangements and block: torch view/permute
-(a different formulation of the same index maps), a tiny case readable by eye,
-the pack/merge consistency on the V channels, and the V-split trick checked
-against one attention with the full value width."""
+"""Pins for the oracle's PSA rearrangements, block and block gradient: torch
+view/permute (a different formulation of the same index maps, forward and
+inverse), a tiny case readable by eye, the pack/merge consistency on the V
+channels, the V-split trick checked against one attention with the full value
+width, and the block gradient against torch fp64 autograd of the block written
+with torch ops and against central finite differences."""
 import numpy as np
 import pytest
 import torch
@@ -81,3 +83,74 @@ def test_block_matches_torch_composite():
     o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=kd ** -0.5)
     want = o.transpose(-1, -2).reshape(b, nh * 2 * kd, h, w)
     np.testing.assert_allclose(out, want.numpy(), atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Backward: the inverse index maps and the block gradient
+
+
+@pytest.mark.parametrize("b,nh,kd,h,w", [(1, 1, 2, 1, 3), (2, 3, 4, 5, 3), (16, 4, 32, 20, 20)])
+def test_merge_backward_matches_torch_permute(b, nh, kd, h, w):
+    g = torch.Generator().manual_seed(2)
+    d_out = torch.randn(b, nh * 2 * kd, h, w, generator=g).to(torch.bfloat16)
+    lo, hi = oracle.psa_merge_backward(d_out, nh, kd)
+    want = d_out.view(b, nh, 2, kd, h * w).permute(2, 0, 1, 4, 3).reshape(2, b * nh, h * w, kd)
+    assert np.array_equal(_bits(lo), _bits(want[0])) and np.array_equal(_bits(hi), _bits(want[1]))
+
+
+@pytest.mark.parametrize("b,nh,kd,h,w", [(1, 1, 1, 1, 2), (2, 3, 4, 5, 3), (16, 4, 32, 20, 20)])
+def test_pack_backward_matches_torch_permute(b, nh, kd, h, w):
+    g = torch.Generator().manual_seed(3)
+    d_packed = torch.randn(4, b * nh, h * w, kd, generator=g).to(torch.float16)
+    got = oracle.psa_pack_backward(d_packed, b, nh, h, w)
+    want = d_packed.view(4, b, nh, h * w, kd).permute(1, 2, 0, 4, 3).reshape(b, nh * 4 * kd, h, w)
+    assert np.array_equal(_bits(got), _bits(want))
+
+
+def test_backward_maps_invert_forward_maps():
+    b, nh, kd, h, w = 2, 3, 4, 3, 5
+    x = _qkv(b, nh, kd, h, w, seed=6)
+    assert np.array_equal(_bits(oracle.psa_pack_backward(oracle.psa_pack(x, nh, kd), b, nh, h, w)), _bits(x))
+    g = torch.Generator().manual_seed(7)
+    lo = torch.randn(b * nh, h * w, kd, generator=g).to(torch.float16)
+    hi = torch.randn(b * nh, h * w, kd, generator=g).to(torch.float16)
+    lo2, hi2 = oracle.psa_merge_backward(oracle.psa_merge(lo, hi, b, nh, kd, h, w), nh, kd)
+    assert np.array_equal(_bits(lo2), _bits(lo)) and np.array_equal(_bits(hi2), _bits(hi))
+
+
+def _torch_block(x, nh, kd):
+    """The block written with torch ops (pack by view/permute, softmax
+    attention per value half, merge by permute), fp64."""
+    b, _, h, w = x.shape
+    t = x.view(b, nh, 4, kd, h * w).transpose(-1, -2)  # [B, nh, 4, N, kd]
+    q, k, v_lo, v_hi = t[:, :, 0], t[:, :, 1], t[:, :, 2], t[:, :, 3]
+    p = torch.softmax(q @ k.transpose(-1, -2).contiguous() * kd ** -0.5, dim=-1)
+    o = torch.stack([p @ v_lo, p @ v_hi], dim=2)        # [B, nh, 2, N, kd]
+    return o.transpose(-1, -2).reshape(b, nh * 2 * kd, h, w)
+
+
+@pytest.mark.parametrize("b,nh,kd,h,w", [(1, 1, 2, 2, 3), (2, 2, 8, 4, 5), (1, 3, 4, 1, 7)])
+def test_block_backward_matches_torch_autograd(b, nh, kd, h, w):
+    x = _qkv(b, nh, kd, h, w, seed=8).double()
+    g = torch.Generator().manual_seed(9)
+    d_out = torch.randn(b, nh * 2 * kd, h, w, generator=g, dtype=torch.float64)
+    got = oracle.psa_block_backward(x, nh, kd, d_out)
+    xr = x.clone().requires_grad_(True)
+    (_torch_block(xr, nh, kd) * d_out).sum().backward()
+    np.testing.assert_allclose(got, xr.grad.numpy(), atol=1e-11)
+
+
+def test_block_backward_finite_differences():
+    b, nh, kd, h, w = 1, 2, 2, 2, 2
+    x = _qkv(b, nh, kd, h, w, seed=10).double()
+    g = torch.Generator().manual_seed(11)
+    d_out = torch.randn(b, nh * 2 * kd, h, w, generator=g, dtype=torch.float64).numpy()
+    grad = oracle.psa_block_backward(x, nh, kd, d_out)
+    xn = x.numpy()
+    eps = 1e-6
+    for idx in [(0, 0, 0, 0), (0, 3, 1, 0), (0, 5, 0, 1), (0, 10, 1, 1), (0, 15, 0, 0)]:
+        xp, xm = xn.copy(), xn.copy()
+        xp[idx] += eps
+        xm[idx] -= eps
+        fd = ((oracle.psa_block(xp, nh, kd) * d_out).sum() - (oracle.psa_block(xm, nh, kd) * d_out).sum()) / (2 * eps)
+        assert abs(fd - grad[idx]) < 1e-7 * max(1.0, abs(fd)), (idx, fd, grad[idx])
