@@ -11,7 +11,8 @@ GPU.
 
 Entry points (same names as the C ABI):
   fa2_fwd, fa2_bwd_delta, fa2_bwd_dq, fa2_bwd_dkdv, psa_pack_qkv, psa_merge_attn,
-  psa_attn_fused, psa_merge_attn_backward, psa_pack_qkv_backward
+  psa_attn_fused, psa_merge_attn_backward, psa_pack_qkv_backward,
+  psa_extract_v_nchw, psa_extract_v_backward
 Compositions of them:
   attention_fwd (= fa2_fwd), attention_bwd (delta -> dkdv -> dq),
   psa_block (pack -> fa2_fwd on V_lo -> fa2_fwd on V_hi -> merge),
@@ -29,7 +30,7 @@ from ._lib import FA2_BF16, FA2_F16, FA2_F32, Fa2Error, library_path, load  # no
 
 __all__ = [
     "fa2_fwd", "fa2_bwd_delta", "fa2_bwd_dq", "fa2_bwd_dkdv", "psa_pack_qkv", "psa_merge_attn", "psa_attn_fused",
-    "psa_merge_attn_backward", "psa_pack_qkv_backward",
+    "psa_merge_attn_backward", "psa_pack_qkv_backward", "psa_extract_v_nchw", "psa_extract_v_backward",
     "attention_fwd", "attention_bwd", "psa_block", "psa_block_backward", "Fa2Error", "load", "library_path",
 ]
 
@@ -292,4 +293,31 @@ def psa_block_backward(d_out, num_heads: int, key_dim: int, workspace: dict):
         fa2_bwd_dkdv(packed[0], packed[1], packed[2 + half], d_o[half], lse, delta, scale, dk_dst, d_packed[2 + half])
         fa2_bwd_dq(packed[0], packed[1], packed[2 + half], d_o[half], lse, delta, scale, dq_dst)
     return psa_pack_qkv_backward(d_packed, b, num_heads, h, w, extra, ws["d_qkv"])
+
+
+def psa_extract_v_nchw(qkv, num_heads: int, key_dim: int, v=None):
+    """qkv [B, nh*4*kd, H, W] -> v [B, nh*2*kd, H, W] (each head's V_lo, V_hi channels)."""
+    _check("qkv", qkv)
+    b, ch, h, w = qkv.shape
+    if ch != num_heads * 4 * key_dim:
+        raise ValueError(f"qkv has {ch} channels, expected num_heads*4*key_dim = {num_heads * 4 * key_dim}")
+    if v is None:
+        v = torch.empty((b, num_heads * 2 * key_dim, h, w), dtype=qkv.dtype, device=qkv.device)
+    _check("v", v, qkv.dtype, (b, num_heads * 2 * key_dim, h, w), qkv.device)
+    _lib.call("psa_extract_v_nchw", _dtype_code(qkv), qkv.data_ptr(), v.data_ptr(), b, num_heads, key_dim, h, w,
+              _stream(qkv.device))
+    return v
+
+
+def psa_extract_v_backward(d_v, d_qkv, num_heads: int, key_dim: int):
+    """Adds d_v [B, nh*2*kd, H, W] into the V channels of d_qkv [B, nh*4*kd, H, W]
+    (in place; call it after psa_pack_qkv_backward). Returns d_qkv."""
+    _check("d_v", d_v)
+    b, ch, h, w = d_v.shape
+    if ch != num_heads * 2 * key_dim:
+        raise ValueError(f"d_v has {ch} channels, expected num_heads*2*key_dim = {num_heads * 2 * key_dim}")
+    _check("d_qkv", d_qkv, d_v.dtype, (b, num_heads * 4 * key_dim, h, w), d_v.device)
+    _lib.call("psa_extract_v_backward", _dtype_code(d_v), d_v.data_ptr(), d_qkv.data_ptr(), b, num_heads, key_dim,
+              h, w, _stream(d_v.device))
+    return d_qkv
 

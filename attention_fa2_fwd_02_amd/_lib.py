@@ -30,6 +30,8 @@ SIGNATURES = {
     "psa_attn_fused": [_int, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _p],
     "psa_merge_attn_backward": [_int, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _p],
     "psa_pack_qkv_backward": [_int, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _p],
+    "psa_extract_v_nchw": [_int, _p, _p, _i32, _i32, _i32, _i32, _i32, _p],
+    "psa_extract_v_backward": [_int, _p, _p, _i32, _i32, _i32, _i32, _i32, _p],
 }
 _RESTYPES = {"fa2_abi_version": _i32, "fa2_status_str": ctypes.c_char_p, "fa2_last_error": ctypes.c_char_p}
 

@@ -198,6 +198,28 @@ fa2_status psa_pack_qkv_backward(fa2_dtype dt, const void *d_packed, const void 
                                                          (hipStream_t)stream));
 }
 
+fa2_status psa_extract_v_nchw(fa2_dtype dt, const void *qkv, void *v, int32_t batch, int32_t num_heads,
+                              int32_t key_dim, int32_t h, int32_t w, void *stream) {
+    static const char fn[] = "psa_extract_v_nchw";
+    fa2_status st = check_psa(fn, dt, batch, num_heads, key_dim, h, w);
+    if (st != FA2_OK) return st;
+    REQUIRE_PTR(fn, qkv);
+    REQUIRE_PTR(fn, v);
+    const fa2mi::PsaShape s{batch, num_heads, key_dim, h * w};
+    return launched(fn, fa2mi::launch_psa_extract_v((int)dt, qkv, v, s, (hipStream_t)stream));
+}
+
+fa2_status psa_extract_v_backward(fa2_dtype dt, const void *d_v, void *d_qkv, int32_t batch, int32_t num_heads,
+                                  int32_t key_dim, int32_t h, int32_t w, void *stream) {
+    static const char fn[] = "psa_extract_v_backward";
+    fa2_status st = check_psa(fn, dt, batch, num_heads, key_dim, h, w);
+    if (st != FA2_OK) return st;
+    REQUIRE_PTR(fn, d_v);
+    REQUIRE_PTR(fn, d_qkv);
+    const fa2mi::PsaShape s{batch, num_heads, key_dim, h * w};
+    return launched(fn, fa2mi::launch_psa_extract_v_backward((int)dt, d_v, d_qkv, s, (hipStream_t)stream));
+}
+
 fa2_status psa_attn_fused(fa2_dtype dt, const void *qkv, void *out, float *lse, int32_t batch,
                           int32_t num_heads, int32_t key_dim, int32_t h, int32_t w, void *stream) {
     static const char fn[] = "psa_attn_fused";

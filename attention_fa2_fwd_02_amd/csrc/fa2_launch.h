@@ -42,6 +42,9 @@ hipError_t launch_psa_merge_backward(int dt, const void *d_out, void *d_lo, void
                                      hipStream_t stream);
 hipError_t launch_psa_pack_backward(int dt, const void *d_packed, const void *d_qk_extra, void *d_qkv,
                                     const PsaShape &s, hipStream_t stream);
+hipError_t launch_psa_extract_v(int dt, const void *qkv, void *v, const PsaShape &s, hipStream_t stream);
+hipError_t launch_psa_extract_v_backward(int dt, const void *d_v, void *d_qkv, const PsaShape &s,
+                                         hipStream_t stream);
 
 // Smallest query rows per forward / dq workgroup and key rows per dkdv
 // workgroup (the ABI checks that the 1-D grids fit in int32).

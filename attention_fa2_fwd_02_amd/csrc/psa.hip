@@ -1,7 +1,7 @@
 // PSA rearrangements around the attention of a C2PSA block (vision_rs
 // psa.rs, "psa_pack_qkv", "psa_merge_attn_nchw" and their backward kernels
-// "psa_pack_qkv_backward", "psa_merge_attn_backward"). All are batched
-// transposes between a channel-major NCHW slice [kd channels][hw pixels] and
+// "psa_pack_qkv_backward", "psa_merge_attn_backward"). The first four are
+// batched transposes between a channel-major NCHW slice [kd channels][hw pixels] and
 // a pixel-major attention operand [hw rows][kd]:
 //   pack : slice (b, head, s) of qkv = channels head*4kd + s*kd .. +kd of
 //          batch b, i.e. the contiguous [kd][hw] block ((b*nh+head)*4+s)*kd*hw,
@@ -12,7 +12,9 @@
 //          (2*bh + half)*kd*hw;
 //   merge backward: the inverse of merge (d_out slices to d_o_lo / d_o_hi);
 //   pack backward : the inverse of pack (d_packed sections to d_qkv slices),
-//          optionally adding a second Q/K gradient pair.
+//          optionally adding a second Q/K gradient pair;
+// and, without a transpose, "psa_extract_v_nchw" and "psa_extract_v_backward"
+// (the V channels of each head as one contiguous block).
 // One workgroup moves a kd x P tile (P pixels) through LDS so that global
 // reads and writes are both contiguous 16-byte vectors.
 #include "fa2_device.h"
@@ -199,6 +201,64 @@ static hipError_t to_channels_by_kd(const SecPtrs &src, const SecPtrs &add, void
         case 32: return to_channels_dispatch<T, 32, NSEC, ADD>(src, add, out, s, st);
         case 64: return to_channels_dispatch<T, 64, NSEC, ADD>(src, add, out, s, st);
         case 128: return to_channels_dispatch<T, 128, NSEC, ADD>(src, add, out, s, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// psa_extract_v_nchw and its backward: per head, the V_lo and V_hi channels
+// are one contiguous block of 2 kd rows of hw pixels both in qkv (channels
+// head*4kd + 2kd ..) and in v (channels head*2kd ..). Block j of src
+// (src + j*src_stride + src_off) is copied to, or with ADD added in fp32 to,
+// block j of dst (dst + j*dst_stride + dst_off); block_vecs 16-byte vectors
+// per block (2 kd hw elements is always a whole number of vectors, and every
+// block starts 16-byte aligned).
+template <typename T, bool ADD>
+__global__ __launch_bounds__(256) void vblock_kernel(const T *__restrict__ src, T *__restrict__ dst,
+                                                     int64_t src_stride, int64_t src_off, int64_t dst_stride,
+                                                     int64_t dst_off, int block_vecs, int chunks) {
+    constexpr int VEC = 16 / (int)sizeof(T);
+    const int j = blockIdx.x / chunks;
+    const int v = (blockIdx.x % chunks) * 256 + threadIdx.x;
+    if (v >= block_vecs) return;
+    const uint4 *s4 = reinterpret_cast<const uint4 *>(src + j * src_stride + src_off) + v;
+    uint4 *d4 = reinterpret_cast<uint4 *>(dst + j * dst_stride + dst_off) + v;
+    uint4 x = *s4;
+    if constexpr (ADD) {
+        const uint4 y = *d4;
+        T *ex = reinterpret_cast<T *>(&x);
+        const T *ey = reinterpret_cast<const T *>(&y);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) ex[i] = static_cast<T>(static_cast<float>(ey[i]) + static_cast<float>(ex[i]));
+    }
+    *d4 = x;
+}
+
+template <typename T, bool ADD>
+static hipError_t vblock_launch(const void *src, void *dst, int64_t src_stride, int64_t src_off, int64_t dst_stride,
+                                int64_t dst_off, const PsaShape &s, hipStream_t stream) {
+    constexpr int VEC = 16 / (int)sizeof(T);
+    const int64_t block_elems = (int64_t)2 * s.key_dim * s.hw;
+    const int block_vecs = (int)(block_elems / VEC);
+    const int chunks = (block_vecs + 255) / 256;
+    const int grid = s.batch * s.num_heads * chunks;
+    hipLaunchKernelGGL((vblock_kernel<T, ADD>), dim3(grid), dim3(256), 0, stream, (const T *)src, (T *)dst,
+                       src_stride, src_off, dst_stride, dst_off, block_vecs, chunks);
+    return hipGetLastError();
+}
+
+hipError_t launch_psa_extract_v(int dt, const void *qkv, void *v, const PsaShape &s, hipStream_t stream) {
+    const int64_t kh = (int64_t)s.key_dim * s.hw;
+    if (dt == 0) return vblock_launch<uint32_t, false>(qkv, v, 4 * kh, 2 * kh, 2 * kh, 0, s, stream);
+    return vblock_launch<uint16_t, false>(qkv, v, 4 * kh, 2 * kh, 2 * kh, 0, s, stream);
+}
+
+hipError_t launch_psa_extract_v_backward(int dt, const void *d_v, void *d_qkv, const PsaShape &s,
+                                         hipStream_t stream) {
+    const int64_t kh = (int64_t)s.key_dim * s.hw;
+    switch (dt) {
+        case 0: return vblock_launch<float, true>(d_v, d_qkv, 2 * kh, 0, 4 * kh, 2 * kh, s, stream);
+        case 1: return vblock_launch<_Float16, true>(d_v, d_qkv, 2 * kh, 0, 4 * kh, 2 * kh, s, stream);
+        case 2: return vblock_launch<__bf16, true>(d_v, d_qkv, 2 * kh, 0, 4 * kh, 2 * kh, s, stream);
         default: return hipErrorInvalidValue;
     }
 }

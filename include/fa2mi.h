@@ -183,13 +183,37 @@ fa2_status psa_merge_attn_backward(fa2_dtype dt, const void *d_out, void *d_o_lo
  * calls' dQ and dK atomically; here the second call's pair is passed
  * separately and added in fp32 before rounding. Without it the result is a
  * bit-exact copy (the inverse permutation of psa_pack_qkv). d_qkv is
- * overwritten entirely (the page accumulates with atomics because a second
- * kernel also adds into the V channels; no such kernel is part of this
- * library). dt is F16, BF16 or F32.
+ * overwritten entirely (the page accumulates with atomics because
+ * psa_extract_v_backward also adds into the V channels; here that call
+ * follows this one on the stream and adds). dt is F16, BF16 or F32.
  */
 fa2_status psa_pack_qkv_backward(fa2_dtype dt, const void *d_packed, const void *d_qk_extra, void *d_qkv,
                                  int32_t batch, int32_t num_heads, int32_t key_dim, int32_t h, int32_t w,
                                  void *stream);
+
+/*
+ * PSA V extraction (vision_rs psa.rs, "psa_extract_v_nchw"): copies the V
+ * channels of the qkv activation [batch, num_heads*4*key_dim, h, w] into v
+ * NCHW [batch, num_heads*2*key_dim, h, w]:
+ *   v[b][hd*2*key_dim + d][n] = qkv[b][hd*4*key_dim + 2*key_dim + d][n],
+ * d < 2*key_dim (V_lo then V_hi). Bit-exact copy.
+ */
+fa2_status psa_extract_v_nchw(fa2_dtype dt, const void *qkv, void *v,
+                              int32_t batch, int32_t num_heads, int32_t key_dim, int32_t h, int32_t w,
+                              void *stream);
+
+/*
+ * Backward of psa_extract_v_nchw (vision_rs psa.rs, "psa_extract_v_backward"):
+ * ADDS the gradient d_v [batch, num_heads*2*key_dim, h, w] into the V
+ * channels of d_qkv [batch, num_heads*4*key_dim, h, w] (fp32 add, one
+ * rounding); the Q and K channels are not touched. The page accumulates
+ * with atomics because psa_pack_qkv_backward writes the same channels; here
+ * the two are ordered on the stream instead: call psa_pack_qkv_backward
+ * (which overwrites d_qkv) first, then this.
+ */
+fa2_status psa_extract_v_backward(fa2_dtype dt, const void *d_v, void *d_qkv,
+                                  int32_t batch, int32_t num_heads, int32_t key_dim, int32_t h, int32_t w,
+                                  void *stream);
 
 #ifdef __cplusplus
 }

@@ -20,6 +20,9 @@ What each routine follows:
     "FlashAttn2PsaRuntimeOp").
   * ``psa_merge_backward`` / ``psa_pack_backward`` - the inverse index maps
     (psa.rs "psa_merge_attn_backward", "psa_pack_qkv_backward").
+  * ``psa_extract_v`` / ``psa_extract_v_backward`` - the V-channel gather of
+    psa.rs "psa_extract_v_nchw" and its adjoint, the scatter of d_v into the
+    V channels of a zero d_qkv ("psa_extract_v_backward").
   * ``psa_block_backward`` - the block's gradient by the chain rule in the
     order of psa.rs's backward: merge backward, the attention gradients of
     both calls (dQ and dK summed over the two calls, as that page's combined
@@ -78,6 +81,7 @@ def _load():
         lib.oracle_psa_merge.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] + [_i64] * 4
         lib.oracle_psa_merge_backward.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] + [_i64] * 4
         lib.oracle_psa_pack_backward.argtypes = [ctypes.c_void_p] * 2 + [ctypes.c_int] + [_i64] * 4
+        lib.oracle_psa_extract_v.argtypes = [ctypes.c_void_p] * 2 + [ctypes.c_int] + [_i64] * 4
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -238,6 +242,32 @@ def psa_block_backward(qkv, num_heads: int, key_dim: int, d_out, threads: int | 
     dq_hi, dk_hi, dv_hi = attention_bwd(packed[0], packed[1], packed[3], d_hi, scale, threads)
     d_packed = np.stack([dq_lo + dq_hi, dk_lo + dk_hi, dv_lo, dv_hi])
     return psa_pack_backward(d_packed, b, num_heads, h, w)
+
+
+def psa_extract_v(qkv, num_heads: int, key_dim: int) -> np.ndarray:
+    """qkv [B, nh*4*kd, H, W] -> v [B, nh*2*kd, H, W], bit-exact copy."""
+    src = _raw(qkv)
+    b, ch, h, w = src.shape
+    if ch != num_heads * 4 * key_dim:
+        raise ValueError("channel count is not num_heads*4*key_dim")
+    out = np.empty((b, num_heads * 2 * key_dim, h, w), src.dtype)
+    rc = _load().oracle_psa_extract_v(src.ctypes.data, out.ctypes.data, src.itemsize, b, num_heads, key_dim, h * w)
+    if rc != 0:
+        raise RuntimeError("oracle_psa_extract_v failed")
+    return out
+
+
+def psa_extract_v_backward(d_v, num_heads: int, key_dim: int) -> np.ndarray:
+    """The gradient of psa_extract_v with respect to qkv for output gradient
+    d_v [B, nh*2*kd, H, W]: d_v in each head's V channels, zero in its Q and K
+    channels. fp64 [B, nh*4*kd, H, W]."""
+    g = _f64(d_v)
+    b, ch, h, w = g.shape
+    if ch != num_heads * 2 * key_dim:
+        raise ValueError("channel count is not num_heads*2*key_dim")
+    out = np.zeros((b, num_heads, 4 * key_dim, h, w), np.float64)
+    out[:, :, 2 * key_dim:] = g.reshape(b, num_heads, 2 * key_dim, h, w)
+    return out.reshape(b, num_heads * 4 * key_dim, h, w)
 
 
 if __name__ == "__main__":  # pragma: no cover

@@ -260,3 +260,21 @@ int oracle_psa_pack_backward(const void *d_packed, void *d_qkv, int esize,
                     }
     return 0;
 }
+
+/* psa_extract_v_nchw: qkv NCHW [B, nh*4*kd, H*W] -> v NCHW [B, nh*2*kd, H*W]:
+ *   v[b][h*2*kd + d][n] = qkv[b][h*4*kd + 2*kd + d][n],  d < 2*kd */
+int oracle_psa_extract_v(const void *qkv, void *v, int esize,
+                         int64_t batch, int64_t nh, int64_t kd, int64_t hw) {
+    if (batch <= 0 || nh <= 0 || kd <= 0 || hw <= 0 || esize <= 0) return -1;
+    const char *src = (const char *)qkv;
+    char *dst = (char *)v;
+    for (int64_t b = 0; b < batch; ++b)
+        for (int64_t h = 0; h < nh; ++h)
+            for (int64_t d = 0; d < 2 * kd; ++d)
+                for (int64_t n = 0; n < hw; ++n) {
+                    int64_t so = (b * nh * 4 * kd + h * 4 * kd + 2 * kd + d) * hw + n;
+                    int64_t dof = (b * nh * 2 * kd + h * 2 * kd + d) * hw + n;
+                    memcpy(dst + dof * esize, src + so * esize, (size_t)esize);
+                }
+    return 0;
+}

@@ -93,6 +93,10 @@ def test_bwd_and_psa_reject_invalid_arguments():
     assert lib.psa_pack_qkv_backward(2, A, MIS, A, 16, 4, 32, 20, 20, None) == INVALID    # extra misaligned
     assert lib.psa_pack_qkv_backward(2, A, None, A, 0, 4, 32, 20, 20, None) == INVALID
     assert lib.psa_pack_qkv_backward(9, A, None, A, 16, 4, 32, 20, 20, None) == INVALID
+    assert lib.psa_extract_v_nchw(1, A, None, 16, 4, 32, 20, 20, None) == INVALID
+    assert lib.psa_extract_v_nchw(1, A, A, 16, 4, 16, 20, 20, None) == UNSUPPORTED
+    assert lib.psa_extract_v_backward(2, MIS, A, 16, 4, 32, 20, 20, None) == INVALID
+    assert lib.psa_extract_v_backward(2, A, A, 16, 4, 32, -1, 20, None) == INVALID
 
 
 def test_binding_refuses_host_tensors():

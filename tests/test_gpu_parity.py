@@ -382,3 +382,30 @@ def test_psa_block_backward(dt, kd, b, nh, h, w):
 def test_psa_block_backward_needs_forward_workspace():
     with pytest.raises(ValueError, match="workspace"):
         fa2.psa_block_backward(torch.zeros(1, 64, 2, 2, dtype=torch.float16, device=DEV), 1, 32, {})
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("kd,b,nh,h,w", [(32, 16, 4, 20, 20), (32, 2, 3, 5, 7), (64, 1, 2, 9, 9),
+                                         (128, 2, 1, 4, 6), (32, 1, 1, 1, 1)])
+def test_psa_extract_v_and_backward(dt, kd, b, nh, h, w):
+    dtype = DTYPES[dt]
+    case = f"psa extract_v {dt} kd={kd} b={b} nh={nh} h={h} w={w}"
+    print(case, flush=True)
+    g = torch.Generator(device="cpu").manual_seed(61 + kd + h * w)
+    qkv = torch.randn(b, nh * 4 * kd, h, w, generator=g).to(DEV, dtype)
+    v = fa2.psa_extract_v_nchw(qkv, nh, kd)
+    torch.cuda.synchronize()
+    bits = (lambda a: a.view(np.int32)) if dt == "f32" else (lambda a: a.view(np.int16))
+    assert np.array_equal(_bitsof(v, dt), bits(oracle.psa_extract_v(qkv, nh, kd)))
+    # backward adds into the V channels of an existing d_qkv, Q/K untouched
+    d_v = torch.randn(b, nh * 2 * kd, h, w, generator=g).to(DEV, dtype)
+    d_qkv = torch.randn(b, nh * 4 * kd, h, w, generator=g).to(DEV, dtype)
+    before = _np(d_qkv)
+    fa2.psa_extract_v_backward(d_v, d_qkv, nh, kd)
+    torch.cuda.synchronize()
+    want = before + oracle.psa_extract_v_backward(d_v, nh, kd)
+    ulp = {torch.float32: 2.0 ** -23, torch.float16: 2.0 ** -10, torch.bfloat16: 2.0 ** -7}[dtype]
+    got = _np(d_qkv)
+    assert np.all(np.abs(got - want) <= ulp * np.maximum(np.abs(want), 2.0 ** -14)), case
+    qk = lambda a: a.reshape(b, nh, 4 * kd, h * w)[:, :, :2 * kd]
+    assert np.array_equal(qk(got), qk(before))

@@ -154,3 +154,30 @@ def test_block_backward_finite_differences():
         xm[idx] -= eps
         fd = ((oracle.psa_block(xp, nh, kd) * d_out).sum() - (oracle.psa_block(xm, nh, kd) * d_out).sum()) / (2 * eps)
         assert abs(fd - grad[idx]) < 1e-7 * max(1.0, abs(fd)), (idx, fd, grad[idx])
+
+
+@pytest.mark.parametrize("b,nh,kd,h,w", [(1, 1, 1, 1, 2), (2, 3, 4, 5, 3), (16, 4, 32, 20, 20)])
+def test_extract_v_matches_torch_narrow(b, nh, kd, h, w):
+    x = _qkv(b, nh, kd, h, w, seed=12)
+    got = oracle.psa_extract_v(x, nh, kd)
+    want = x.view(b, nh, 4 * kd, h, w)[:, :, 2 * kd:].reshape(b, nh * 2 * kd, h, w)
+    assert np.array_equal(_bits(got), _bits(want))
+
+
+def test_extract_v_backward_matches_torch_autograd():
+    b, nh, kd, h, w = 2, 3, 4, 3, 5
+    x = _qkv(b, nh, kd, h, w, seed=13).double().requires_grad_(True)
+    g = torch.Generator().manual_seed(14)
+    d_v = torch.randn(b, nh * 2 * kd, h, w, generator=g, dtype=torch.float64)
+    v = x.view(b, nh, 4 * kd, h, w)[:, :, 2 * kd:].reshape(b, nh * 2 * kd, h, w)
+    (v * d_v).sum().backward()
+    got = oracle.psa_extract_v_backward(d_v, nh, kd)
+    assert np.array_equal(got, x.grad.numpy())
+
+
+def test_extract_v_equals_merge_of_packed_v_sections():
+    b, nh, kd, h, w = 2, 2, 4, 3, 3
+    x = _qkv(b, nh, kd, h, w, seed=15)
+    packed = oracle.psa_pack(x, nh, kd)
+    merged = oracle.psa_merge(packed[2], packed[3], b, nh, kd, h, w)
+    assert np.array_equal(_bits(oracle.psa_extract_v(x, nh, kd)), _bits(merged))
