@@ -262,6 +262,83 @@ def test_bwd_deterministic():
 
 
 # ---------------------------------------------------------------------------
+# Edge cases: extreme scores, degenerate inputs at full size, maximum sizes
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwd_bwd_peaked_softmax(dt, d):
+    """scale 8/sqrt(d): scaled scores with a spread of ~8, nearly one-hot rows;
+    the reference max moves often and most probabilities underflow. dO is
+    scaled by 1/16 (rounded once, the same tensor on both sides) so that the
+    gradients stay O(1), where the absolute bar is meaningful: at scale 1 they
+    reach ~26, whose half-ulp in bfloat16 alone exceeds 2e-2."""
+    bh, nq, nk = 2, 150, 333
+    case = f"peaked {dt} d={d}"
+    print(case, flush=True)
+    x = _inputs(dt, bh, nq, nk, d, seed=300 + d, with_do=True)
+    x["do"] = (x["do"].float() / 16).to(x["do"].dtype)
+    scale = 8 / math.sqrt(d)
+    o, lse = fa2.fa2_fwd(x["q"], x["k"], x["v"], scale)
+    dq, dk, dv = fa2.attention_bwd(x["q"], x["k"], x["v"], o, x["do"], lse, scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_fwd(x["q"], x["k"], x["v"], scale)
+    tol = TOL[DTYPES[dt]]
+    _err("O", _np(o), o_ref, tol, case)
+    _err("LSE", _np(lse), lse_ref, tol, case)
+    ref = oracle.attention_bwd(x["q"], x["k"], x["v"], x["do"], scale)
+    for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        _err(name, _np(got), want, tol, case)
+
+
+def test_fwd_degenerate_inputs_full_length():
+    """At the LLM sequence length with the 8-wave launch: Q = 0 and identical
+    keys both make every row uniform, so O is the mean of V over the keys and
+    LSE = scale q.k_0 + ln n_k (checked on every row, no oracle needed)."""
+    bh, n, d = 32, 4096, 128
+    x = _inputs("bf16", bh, n, n, d, seed=17)
+    vmean = x["v"].double().mean(dim=1, keepdim=True)          # [bh, 1, d]
+    # Q = 0
+    q0 = torch.zeros_like(x["q"])
+    o, lse = fa2.fa2_fwd(q0, x["k"], x["v"])
+    torch.cuda.synchronize()
+    assert (o.double() - vmean).abs().max().item() <= 2e-2
+    assert (lse.double() - math.log(n)).abs().max().item() <= 1e-4
+    # every key equal to key 0 of its head
+    k0 = x["k"][:, :1, :].expand(-1, n, -1).contiguous()
+    o, lse = fa2.fa2_fwd(x["q"], k0, x["v"])
+    torch.cuda.synchronize()
+    assert (o.double() - vmean).abs().max().item() <= 2e-2
+    want = (x["q"].double() @ k0[:, :1, :].double().transpose(1, 2)).squeeze(-1) / math.sqrt(d) + math.log(n)
+    assert (lse.double() - want).abs().max().item() <= 2e-3
+
+
+def test_fwd_max_head_size():
+    """One head whose K and V are just under the 2 GiB per-tensor limit of the
+    ABI (n_k = 2^23 - 5 rows of 128 bf16): buffer offsets reach the top of
+    their 32-bit range and the last key tile is ragged."""
+    w = workloads.AttnWorkload("maxhead", 1, 4, (1 << 23) - 5, 128, "bf16", seed=19)
+    x = workloads.attn_inputs(w, device=DEV)
+    o, lse = fa2.fa2_fwd(x["q"], x["k"], x["v"], w.scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_fwd(x["q"], x["k"], x["v"], w.scale)
+    _err("O", _np(o), o_ref, 2e-2, w.name)
+    _err("LSE", _np(lse), lse_ref, 2e-2, w.name)
+
+
+def test_bwd_long_keys():
+    """Backward over a million keys per head (ragged last tile)."""
+    w = workloads.AttnWorkload("longkeys", 2, 4, (1 << 20) + 3, 64, "bf16", seed=23, backward=True)
+    x = workloads.attn_inputs(w, device=DEV)
+    o, lse = fa2.fa2_fwd(x["q"], x["k"], x["v"], w.scale)
+    dq, dk, dv = fa2.attention_bwd(x["q"], x["k"], x["v"], o, x["do"], lse, w.scale)
+    torch.cuda.synchronize()
+    ref = oracle.attention_bwd(x["q"], x["k"], x["v"], x["do"], w.scale)
+    for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        _err(name, _np(got), want, 2e-2, w.name)
+
+
+# ---------------------------------------------------------------------------
 # Fused PSA forward (one kernel, NCHW in and out)
 
 
