@@ -255,15 +255,6 @@ struct TileStage {
 };
 
 // ---------------------------------------------------------------------------
-// Direct global -> LDS load of 16 bytes per lane (gfx950
-// global_load_lds_dwordx4): lane l of the wave writes the 16 bytes at its own
-// global address `g` to LDS at `lds_base + 16 l`; lds_base must be the same
-// for every lane of the instruction.
-__device__ __forceinline__ void load_lds16(const void *g, void *lds_base) {
-    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
-}
-
-// ---------------------------------------------------------------------------
 // Buffer resources: a raw buffer over one head's rows. Loads at byte offsets
 // at or past `bytes` return zero (hardware range check), which zero-fills the
 // rows of a ragged last tile without branches.
@@ -330,68 +321,6 @@ __device__ __forceinline__ typename Traits<DT>::frag ld_vt_frag_tr(const typenam
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 8 * LD));
     typedef short i16x8 __attribute__((ext_vector_type(8)));
-    const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(typename Traits<DT>::frag, both);
-}
-
-// ---------------------------------------------------------------------------
-// XOR-swizzled row-major tiles of 16-bit elements (rows of D elements, no
-// padding): 16-byte chunk c of row r is stored at chunk position c ^ f(r).
-// The gfx950 LDS behaves as 64 four-byte banks; ds_read_b128 serves 16 lanes
-// per cycle (here: 16 consecutive rows, one chunk each) and
-// ds_read_b64_tr_b16 32 lanes per cycle (here: 4 consecutive rows starting
-// at a multiple of 4, 64 contiguous bytes each). f is chosen so that both
-// patterns touch every bank at most once:
-//   D = 128 (one row per 256-byte bank cycle): f = 4*(r%4) + (r/4)%4
-//   D = 64  (two rows per cycle):              f = 4*((r/2)%2) + (r/4)%4
-//   D = 32  (four rows per cycle):             f = (r/4)%4
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-    if constexpr (D == 128) return 4 * (row & 3) + ((row >> 2) & 3);
-    else if constexpr (D == 64) return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
-    else return (row >> 2) & 3;
-}
-
-// Element offset of (row, col) in a swizzled tile.
-template <int D>
-__device__ __forceinline__ int swz_off(int row, int col) {
-    return row * D + ((((col >> 3) ^ swz<D>(row))) << 3) + (col & 7);
-}
-
-// RowStage pieces -> swizzled tile.
-template <Dt DT, int R, int D, int NT>
-__device__ __forceinline__ void store_swizzled(const RowStage<DT, R, D, NT> &st, typename Traits<DT>::elem *lds,
-                                               int tid) {
-    using S = RowStage<DT, R, D, NT>;
-#pragma unroll
-    for (int i = 0; i < S::PER_THREAD; ++i) {
-        const int pc = tid + i * NT;
-        const int row = pc / (D / S::VEC), cv = pc % (D / S::VEC);
-        if (S::PIECES % NT == 0 || pc < S::PIECES)
-            *reinterpret_cast<uint4 *>(lds + row * D + ((cv ^ swz<D>(row)) << 3)) = st.v[i];
-    }
-}
-
-// Row fragment (contraction step t, lane half h) of row `row` of a swizzled tile.
-template <Dt DT, int D>
-__device__ __forceinline__ typename Traits<DT>::frag ld_row_frag_swz(const typename Traits<DT>::elem *tile, int row,
-                                                                     int t, int h) {
-    return *reinterpret_cast<const typename Traits<DT>::frag *>(tile + row * D + (((2 * t + h) ^ swz<D>(row)) << 3));
-}
-
-// Transposed fragment (as ld_vt_frag_tr) from a swizzled tile.
-template <Dt DT, int D>
-__device__ __forceinline__ typename Traits<DT>::frag ld_vt_frag_tr_swz(const typename Traits<DT>::elem *tile, int key0,
-                                                                       int d0, int lane) {
-    static_assert(Traits<DT>::KPL == 8, "16-bit element types only");
-    typedef short i16x4 __attribute__((ext_vector_type(4)));
-    typedef short i16x8 __attribute__((ext_vector_type(8)));
-    using lds_i16x4 = __attribute__((address_space(3))) i16x4;
-    const int l = lane & 15, g = lane >> 4, hh = g >> 1;
-    const int row = key0 + 4 * hh + (l >> 2);
-    const int c = d0 + 16 * (g & 1) + 4 * (l & 3);
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(tile + swz_off<D>(row, c)));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(tile + swz_off<D>(row + 8, c)));
     const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(typename Traits<DT>::frag, both);
 }
