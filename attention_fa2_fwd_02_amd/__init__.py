@@ -10,7 +10,7 @@ every function raises if the library is missing or the tensors are not on a
 GPU.
 
 Entry points (same names as the C ABI):
-  fa2_fwd, fa2_bwd_delta, fa2_bwd_dq, fa2_bwd_dkdv, psa_pack_qkv, psa_merge_attn,
+  fa2_fwd, fa2_fwd_splitkv_plan, fa2_fwd_splitkv, fa2_bwd_delta, fa2_bwd_dq, fa2_bwd_dkdv, psa_pack_qkv, psa_merge_attn,
   psa_attn_fused, psa_merge_attn_backward, psa_pack_qkv_backward,
   psa_extract_v_nchw, psa_extract_v_backward
 Compositions of them:
@@ -21,6 +21,7 @@ Compositions of them:
 """
 from __future__ import annotations
 
+import ctypes
 import math
 
 import torch
@@ -29,7 +30,7 @@ from . import _lib
 from ._lib import FA2_BF16, FA2_F16, FA2_F32, Fa2Error, library_path, load  # noqa: F401
 
 __all__ = [
-    "fa2_fwd", "fa2_bwd_delta", "fa2_bwd_dq", "fa2_bwd_dkdv", "psa_pack_qkv", "psa_merge_attn", "psa_attn_fused",
+    "fa2_fwd", "fa2_fwd_splitkv_plan", "fa2_fwd_splitkv", "fa2_bwd_delta", "fa2_bwd_dq", "fa2_bwd_dkdv", "psa_pack_qkv", "psa_merge_attn", "psa_attn_fused",
     "psa_merge_attn_backward", "psa_pack_qkv_backward", "psa_extract_v_nchw", "psa_extract_v_backward",
     "attention_fwd", "attention_bwd", "psa_block", "psa_block_backward", "Fa2Error", "load", "library_path",
 ]
@@ -83,6 +84,51 @@ def fa2_fwd(q, k, v, scale=None, o=None, lse=None):
     _check("lse", lse, torch.float32, (bh, n_q), dev)
     _lib.call("fa2_fwd", _dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
               lse.data_ptr(), bh, n_q, n_k, d, _scale(scale, d), _stream(dev))
+    return o, lse
+
+
+def fa2_fwd_splitkv_plan(dtype, bh, n_q, n_k, head_dim, num_splits=0):
+    """(splits used, workspace bytes) of fa2_fwd_splitkv for these sizes.
+
+    Host-only: needs the library but no GPU. num_splits 0 lets the library
+    choose; a request is clamped to one range per 64 keys.
+    """
+    try:
+        code = _DT[dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {dtype}; use float32, float16 or bfloat16") from None
+    splits = ctypes.c_int32()
+    nbytes = ctypes.c_int64()
+    _lib.call("fa2_fwd_splitkv_plan", code, bh, n_q, n_k, head_dim, num_splits, ctypes.addressof(splits),
+              ctypes.addressof(nbytes))
+    return splits.value, nbytes.value
+
+
+def fa2_fwd_splitkv(q, k, v, scale=None, num_splits=0, workspace=None, o=None, lse=None):
+    """Key-split forward: the same (o, lse) as fa2_fwd, with each head's keys
+    cut into ranges processed by separate workgroups and merged by their
+    log-sum-exp. For few query rows per head (decoding). `workspace` is an
+    optional uint8 GPU tensor of at least fa2_fwd_splitkv_plan's size
+    (allocated here when omitted)."""
+    _check("q", q)
+    bh, n_q, d = q.shape
+    n_k = k.shape[1]
+    dev = q.device
+    _check("k", k, q.dtype, (bh, n_k, d), dev)
+    _check("v", v, q.dtype, (bh, n_k, d), dev)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((bh, n_q), dtype=torch.float32, device=dev)
+    _check("o", o, q.dtype, q.shape, dev)
+    _check("lse", lse, torch.float32, (bh, n_q), dev)
+    _, need = fa2_fwd_splitkv_plan(q.dtype, bh, n_q, n_k, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _check("workspace", workspace, torch.uint8, None, dev)
+    _lib.call("fa2_fwd_splitkv", _dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+              lse.data_ptr(), workspace.data_ptr(), workspace.numel(), bh, n_q, n_k, d, _scale(scale, d),
+              num_splits, _stream(dev))
     return o, lse
 
 

@@ -22,6 +22,8 @@ SIGNATURES = {
     "fa2_status_str": [_int],
     "fa2_last_error": [],
     "fa2_fwd": [_int, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i32, _f32, _p],
+    "fa2_fwd_splitkv_plan": [_int, _i64, _i64, _i64, _i32, _i32, _p, _p],
+    "fa2_fwd_splitkv": [_int, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _f32, _i32, _p],
     "fa2_bwd_delta": [_int, _p, _p, _p, _i64, _i64, _i32, _p],
     "fa2_bwd_dq": [_int, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i32, _f32, _p],
     "fa2_bwd_dkdv": [_int, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i32, _f32, _p],

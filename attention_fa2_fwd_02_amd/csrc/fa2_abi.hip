@@ -71,6 +71,41 @@ fa2_status check_psa(const char *fn, fa2_dtype dt, int32_t batch, int32_t num_he
 
 }  // namespace
 
+namespace fa2mi {
+
+SplitPlan plan_splitkv(int64_t bh, int64_t n_q, int64_t n_k, int head_dim, int requested) {
+    SplitPlan p{};
+    p.waves = n_q <= 64 ? 2 : n_q <= 128 ? 4 : 8;
+    const int64_t rows = 32 * p.waves;
+    const int64_t blocks = bh * ((n_q + rows - 1) / rows);
+    const int64_t tiles = (n_k + kSplitKeyAlign - 1) / kSplitKeyAlign;
+    int64_t want = requested;
+    if (want <= 0) {
+        // one workgroup per CU measured fastest (more ranges add prologue,
+        // epilogue and combine work without more bandwidth)
+        constexpr int64_t kTargetBlocks = 256, kMinKeys = 256;
+        want = (kTargetBlocks + blocks - 1) / blocks;
+        const int64_t cap = (n_k + kMinKeys - 1) / kMinKeys;
+        if (want > cap) want = cap;
+    }
+    if (want > tiles) want = tiles;
+    if (want < 1) want = 1;
+    const int64_t per = (n_k + want - 1) / want;
+    const int64_t len = (per + kSplitKeyAlign - 1) / kSplitKeyAlign * kSplitKeyAlign;
+    p.split_len = (int)len;
+    p.nsplit = (int)((n_k + len - 1) / len);
+    if (p.nsplit == 1) {
+        p.ws_bytes = 0;
+    } else if (p.nsplit > INT_MAX / blocks || bh * n_q / 8 > INT_MAX) {
+        p.ws_bytes = -1;  // the partial or the combine grid does not fit
+    } else {
+        p.ws_bytes = (int64_t)p.nsplit * bh * n_q * (head_dim + 1) * (int64_t)sizeof(float);
+    }
+    return p;
+}
+
+}  // namespace fa2mi
+
 extern "C" {
 
 int32_t fa2_abi_version(void) { return 1; }
@@ -99,6 +134,46 @@ fa2_status fa2_fwd(fa2_dtype dt, const void *q, const void *k, const void *v, vo
     REQUIRE_PTR(fn, lse);
     const fa2mi::AttnShape s{bh, (int)n_q, (int)n_k, head_dim, scale};
     return launched(fn, fa2mi::launch_fwd((int)dt, q, k, v, o, lse, s, (hipStream_t)stream));
+}
+
+fa2_status fa2_fwd_splitkv_plan(fa2_dtype dt, int64_t bh, int64_t n_q, int64_t n_k, int32_t head_dim,
+                                int32_t num_splits, int32_t *splits_used, int64_t *workspace_bytes) {
+    static const char fn[] = "fa2_fwd_splitkv_plan";
+    fa2_status st = check_attn(fn, dt, bh, n_q, n_k, head_dim, 1.f, fa2mi::kFwdRowsPerBlock, n_q);
+    if (st != FA2_OK) return st;
+    if (num_splits < 0) return fail(FA2_ERR_INVALID_ARG, fn, "num_splits must be >= 0 (0 picks it)");
+    if (splits_used == nullptr || workspace_bytes == nullptr)
+        return fail(FA2_ERR_INVALID_ARG, fn, "splits_used and workspace_bytes must not be NULL");
+    const fa2mi::SplitPlan p = fa2mi::plan_splitkv(bh, n_q, n_k, head_dim, num_splits);
+    if (p.ws_bytes < 0) return fail(FA2_ERR_INVALID_ARG, fn, "grid exceeds 2^31 - 1 workgroups");
+    *splits_used = p.nsplit;
+    *workspace_bytes = p.ws_bytes;
+    g_last_error[0] = '\0';
+    return FA2_OK;
+}
+
+fa2_status fa2_fwd_splitkv(fa2_dtype dt, const void *q, const void *k, const void *v, void *o, float *lse,
+                           void *workspace, int64_t workspace_bytes, int64_t bh, int64_t n_q, int64_t n_k,
+                           int32_t head_dim, float scale, int32_t num_splits, void *stream) {
+    static const char fn[] = "fa2_fwd_splitkv";
+    fa2_status st = check_attn(fn, dt, bh, n_q, n_k, head_dim, scale, fa2mi::kFwdRowsPerBlock, n_q);
+    if (st != FA2_OK) return st;
+    if (num_splits < 0) return fail(FA2_ERR_INVALID_ARG, fn, "num_splits must be >= 0 (0 picks it)");
+    REQUIRE_PTR(fn, q);
+    REQUIRE_PTR(fn, k);
+    REQUIRE_PTR(fn, v);
+    REQUIRE_PTR(fn, o);
+    REQUIRE_PTR(fn, lse);
+    const fa2mi::SplitPlan p = fa2mi::plan_splitkv(bh, n_q, n_k, head_dim, num_splits);
+    if (p.ws_bytes < 0) return fail(FA2_ERR_INVALID_ARG, fn, "grid exceeds 2^31 - 1 workgroups");
+    if (p.ws_bytes > 0) {
+        REQUIRE_PTR(fn, workspace);
+        if (workspace_bytes < p.ws_bytes)
+            return fail(FA2_ERR_INVALID_ARG, fn, "workspace_bytes is below the size fa2_fwd_splitkv_plan reports");
+    }
+    const fa2mi::AttnShape s{bh, (int)n_q, (int)n_k, head_dim, scale};
+    return launched(fn, fa2mi::launch_fwd_splitkv((int)dt, q, k, v, o, lse, static_cast<float *>(workspace), s, p,
+                                                  (hipStream_t)stream));
 }
 
 fa2_status fa2_bwd_delta(fa2_dtype dt, const void *o, const void *d_o, float *delta, int64_t bh, int64_t n_q,

@@ -140,7 +140,6 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     constexpr int BR = 32 * WAVES;
     constexpr int KPL = Tr::KPL;
     constexpr int KSTEP = 2 * KPL;
-    constexpr int VEC = vec_elems<DT>();
     using Tl = BwdTile<DT, D>;
     constexpr int LDT = BC + 4;          // float32 transposed K copy
     constexpr int KS = BC * Tl::LD;
@@ -274,7 +273,6 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     constexpr int BKV = 32 * WAVES;
     constexpr int KPL = Tr::KPL;
     constexpr int KSTEP = 2 * KPL;
-    constexpr int VEC = vec_elems<DT>();
     using Tl = BwdTile<DT, D>;
     constexpr int LDT = BQ + 4;          // float32 transposed copies
     constexpr int QS = BQ * Tl::LD;

@@ -153,11 +153,17 @@ __device__ __forceinline__ void fwd_tile(const typename Traits<DT>::elem *kt, co
 
 }
 
-template <Dt DT, int D, int BC, int WAVES>
+// PARTIAL: key-split mode. The key rows of a head are cut into nsplit
+// consecutive ranges of split_len rows (a multiple of BC; the last range may
+// be shorter); workgroup (bh, split, query block) runs the recurrence over
+// its range only and writes the range's normalised output in float32 to
+// O = Opart[nsplit][bh][n_q][D] and its log2-sum-exp, m + log2 l, to
+// LSE = Lpart[nsplit][bh][n_q]. splitkv_combine_kernel merges the ranges.
+template <Dt DT, int D, int BC, int WAVES, bool PARTIAL>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(
     const typename Traits<DT>::elem *__restrict__ Q, const typename Traits<DT>::elem *__restrict__ K,
-    const typename Traits<DT>::elem *__restrict__ V, typename Traits<DT>::elem *__restrict__ O,
-    float *__restrict__ LSE, int n_q, int n_k, int n_qblocks, int total_blocks, float scale_log2) {
+    const typename Traits<DT>::elem *__restrict__ V, void *__restrict__ O, float *__restrict__ LSE, int n_q,
+    int n_k, int n_qblocks, int total_blocks, float scale_log2, int nsplit, int split_len) {
     using Tr = Traits<DT>;
     using elem = typename Tr::elem;
     using frag = typename Tr::frag;
@@ -171,10 +177,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     constexpr int LDV = fwd_ldv<DT, D, BC>();
     constexpr int KS = BC * LDK;            // elements per K stage
     constexpr int VS = TR ? BC * LDV : D * LDV;
-    constexpr int NKB = BC / 32;            // 32-key blocks per tile
     constexpr int NDB = D / 32;             // 32-row blocks of O^T
     constexpr int TS = D / KSTEP;           // contraction steps over head_dim
-    constexpr int TP = 32 / KSTEP;          // contraction steps per 32-key block
     static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
 
     __shared__ __attribute__((aligned(16))) elem Ks[2 * KS];
@@ -183,10 +187,24 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, col = lane & 31;
     const int blk = xcd_remap(blockIdx.x, total_blocks);
-    const int bh = blk / n_qblocks, qb = blk % n_qblocks;
+    // Block order: query block fastest, then split, then head, so the
+    // workgroups that share one key range sit next to each other (same XCD,
+    // same L2).
+    int bh, qb, split = 0, kbeg = 0, klen = n_k;
+    if constexpr (PARTIAL) {
+        qb = blk % n_qblocks;
+        const int rest = blk / n_qblocks;
+        split = rest % nsplit;
+        bh = rest / nsplit;
+        kbeg = split * split_len;
+        klen = min(split_len, n_k - kbeg);
+    } else {
+        bh = blk / n_qblocks;
+        qb = blk % n_qblocks;
+    }
     const int qrow = qb * BR + wave * 32 + col;
     const int64_t qoff = (int64_t)bh * n_q * D;
-    const int64_t koff = (int64_t)bh * n_k * D;
+    const int64_t koff = ((int64_t)bh * n_k + kbeg) * D;
 
     frag qf[TS];
     if (qrow < n_q) {
@@ -207,7 +225,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 
     // K/V tiles: buffer loads over this head's rows (rows past n_k read as
     // zero) into registers, then into one of two LDS stages.
-    const uint32_t head_bytes = (uint32_t)n_k * D * (uint32_t)sizeof(elem);
+    const uint32_t head_bytes = (uint32_t)klen * D * (uint32_t)sizeof(elem);
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + koff, head_bytes);
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + koff, head_bytes);
     RowStage<DT, BC, D, NT> kst;
@@ -218,7 +236,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
         if constexpr (TR)
             vst.load(vrs, row0, tid);
         else
-            vst.load(V + koff + (int64_t)row0 * D, n_k - row0, tid);
+            vst.load(V + koff + (int64_t)row0 * D, klen - row0, tid);
     };
     auto vstore = [&](elem *dst) {
         if constexpr (TR)
@@ -227,8 +245,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
             vst.template store_transposed<LDV>(dst, tid);
     };
 
-    const int ntiles = (n_k + BC - 1) / BC;
-    const int nfull = n_k / BC;  // full tiles; a ragged last one follows when n_k % BC != 0
+    const int ntiles = (klen + BC - 1) / BC;
+    const int nfull = klen / BC;  // full tiles; a ragged last one follows when klen % BC != 0
     kst.load(krs, 0, tid);
     vload(0);
     kst.template store<LDK>(Ks, tid);
@@ -258,18 +276,61 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     }
     if (nfull < ntiles)
         fwd_tile<DT, D, BC, true>(Ks + (nfull & 1) * KS, Vs + (nfull & 1) * VS, qf, acc, m_ref, l_run, scale_log2,
-                                  n_k - nfull * BC, lane);
+                                  klen - nfull * BC, lane);
 
     const float l_tot = xhalf_sum(l_run);
     if (qrow < n_q) {
         const float inv = 1.f / l_tot;
-        elem *op = O + qoff + (int64_t)qrow * D;
+        if constexpr (PARTIAL) {
+            const int bh_count = total_blocks / (n_qblocks * nsplit);
+            const int64_t prow = ((int64_t)split * bh_count + bh) * n_q + qrow;
+            float *op = static_cast<float *>(O) + prow * D;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) store4<DT>(op + 32 * db + 8 * g + 4 * h, acc[db], g, inv);
-        if (h == 0) LSE[(int64_t)bh * n_q + qrow] = (m_ref + __log2f(l_tot)) * kLn2;
+                for (int g = 0; g < 4; ++g) store4<Dt::F32>(op + 32 * db + 8 * g + 4 * h, acc[db], g, inv);
+            if (h == 0) LSE[prow] = m_ref + __log2f(l_tot);
+        } else {
+            elem *op = static_cast<elem *>(O) + qoff + (int64_t)qrow * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) store4<DT>(op + 32 * db + 8 * g + 4 * h, acc[db], g, inv);
+            if (h == 0) LSE[(int64_t)bh * n_q + qrow] = (m_ref + __log2f(l_tot)) * kLn2;
+        }
     }
+}
+
+// Merge of a key-split forward's ranges (the log-sum-exp combination of
+// partial softmax results; exact up to rounding). Per query row, with L_s the
+// log2-sum-exp of range s and O_s its normalised output:
+//   L = log2 sum_s 2^(L_s),  O = sum_s 2^(L_s - L) O_s,  lse = ln2 * L.
+// D/4 threads per row, 4 consecutive columns each.
+template <Dt DT, int D>
+__global__ __launch_bounds__(256) void splitkv_combine_kernel(const float *__restrict__ Opart,
+                                                              const float *__restrict__ Lpart,
+                                                              typename Traits<DT>::elem *__restrict__ O,
+                                                              float *__restrict__ LSE, int64_t rows, int nsplit) {
+    constexpr int TPR = D / 4;
+    constexpr int RPB = 256 / TPR;
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+    const int c0 = (threadIdx.x % TPR) * 4;
+    if (row >= rows) return;
+    float mx = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, Lpart[s * rows + row]);
+    float sum = 0.f;
+    f32x16 acc = zero16();  // only entries 0..3 are used (store4 group 0)
+    for (int s = 0; s < nsplit; ++s) {
+        const float w = exp2f(Lpart[s * rows + row] - mx);
+        const float4 o = *reinterpret_cast<const float4 *>(Opart + (s * rows + row) * D + c0);
+        sum += w;
+        acc[0] = __builtin_fmaf(w, o.x, acc[0]);
+        acc[1] = __builtin_fmaf(w, o.y, acc[1]);
+        acc[2] = __builtin_fmaf(w, o.z, acc[2]);
+        acc[3] = __builtin_fmaf(w, o.w, acc[3]);
+    }
+    store4<DT>(O + row * D + c0, acc, 0, 1.f / sum);
+    if (c0 == 0) LSE[row] = (mx + log2f(sum)) * kLn2;
 }
 
 template <Dt DT, int D, int WAVES>
@@ -280,8 +341,9 @@ static hipError_t fwd_launch(const void *q, const void *k, const void *v, void *
     const int nqb = (s.n_q + BR - 1) / BR;
     const int total = (int)(s.bh * nqb);
     const float scale_log2 = (float)((double)s.scale * 1.4426950408889634);
-    hipLaunchKernelGGL((fwd_kernel<DT, D, BC, WAVES>), dim3(total), dim3(WAVES * 64), 0, stream, (const elem *)q,
-                       (const elem *)k, (const elem *)v, (elem *)o, lse, s.n_q, s.n_k, nqb, total, scale_log2);
+    hipLaunchKernelGGL((fwd_kernel<DT, D, BC, WAVES, false>), dim3(total), dim3(WAVES * 64), 0, stream,
+                       (const elem *)q, (const elem *)k, (const elem *)v, o, lse, s.n_q, s.n_k, nqb, total,
+                       scale_log2, 1, s.n_k);
     return hipGetLastError();
 }
 
@@ -295,6 +357,64 @@ static hipError_t fwd_dispatch(const void *q, const void *k, const void *v, void
     if (s.bh * ((s.n_q + 255) / 256) >= 2 * kCus) return fwd_launch<DT, D, 8>(q, k, v, o, lse, s, stream);
     if (s.bh * ((s.n_q + 127) / 128) >= kCus) return fwd_launch<DT, D, 4>(q, k, v, o, lse, s, stream);
     return fwd_launch<DT, D, 2>(q, k, v, o, lse, s, stream);
+}
+
+// Key-split forward: partial pass over sp.nsplit key ranges into the
+// workspace, then the combine pass into o and lse.
+template <Dt DT, int D, int WAVES>
+static hipError_t splitkv_launch(const void *q, const void *k, const void *v, void *o, float *lse, float *ws,
+                                 const AttnShape &s, const SplitPlan &sp, hipStream_t stream) {
+    using elem = typename Traits<DT>::elem;
+    constexpr int BC = 64, BR = 32 * WAVES;
+    static_assert(BC == kSplitKeyAlign, "key ranges must start on tile boundaries");
+    const int nqb = (s.n_q + BR - 1) / BR;
+    const int total = (int)(s.bh * nqb * sp.nsplit);
+    const float scale_log2 = (float)((double)s.scale * 1.4426950408889634);
+    const int64_t rows = s.bh * s.n_q;
+    float *opart = ws;
+    float *lpart = ws + (int64_t)sp.nsplit * rows * D;
+    hipLaunchKernelGGL((fwd_kernel<DT, D, BC, WAVES, true>), dim3(total), dim3(WAVES * 64), 0, stream,
+                       (const elem *)q, (const elem *)k, (const elem *)v, (void *)opart, lpart, s.n_q, s.n_k, nqb,
+                       total, scale_log2, sp.nsplit, sp.split_len);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    constexpr int RPB = 256 / (D / 4);
+    hipLaunchKernelGGL((splitkv_combine_kernel<DT, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
+                       stream, (const float *)opart, (const float *)lpart, (elem *)o, lse, rows, sp.nsplit);
+    return hipGetLastError();
+}
+
+template <Dt DT, int D>
+static hipError_t splitkv_dispatch(const void *q, const void *k, const void *v, void *o, float *lse, float *ws,
+                                   const AttnShape &s, const SplitPlan &sp, hipStream_t stream) {
+    if (sp.nsplit == 1) return fwd_dispatch<DT, D>(q, k, v, o, lse, s, stream);
+    switch (sp.waves) {
+        case 2: return splitkv_launch<DT, D, 2>(q, k, v, o, lse, ws, s, sp, stream);
+        case 4: return splitkv_launch<DT, D, 4>(q, k, v, o, lse, ws, s, sp, stream);
+        case 8: return splitkv_launch<DT, D, 8>(q, k, v, o, lse, ws, s, sp, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <Dt DT>
+static hipError_t splitkv_by_dim(const void *q, const void *k, const void *v, void *o, float *lse, float *ws,
+                                 const AttnShape &s, const SplitPlan &sp, hipStream_t stream) {
+    switch (s.head_dim) {
+        case 32: return splitkv_dispatch<DT, 32>(q, k, v, o, lse, ws, s, sp, stream);
+        case 64: return splitkv_dispatch<DT, 64>(q, k, v, o, lse, ws, s, sp, stream);
+        case 128: return splitkv_dispatch<DT, 128>(q, k, v, o, lse, ws, s, sp, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_fwd_splitkv(int dt, const void *q, const void *k, const void *v, void *o, float *lse, float *ws,
+                              const AttnShape &s, const SplitPlan &sp, hipStream_t stream) {
+    switch (dt) {
+        case 0: return splitkv_by_dim<Dt::F32>(q, k, v, o, lse, ws, s, sp, stream);
+        case 1: return splitkv_by_dim<Dt::F16>(q, k, v, o, lse, ws, s, sp, stream);
+        case 2: return splitkv_by_dim<Dt::BF16>(q, k, v, o, lse, ws, s, sp, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <Dt DT>

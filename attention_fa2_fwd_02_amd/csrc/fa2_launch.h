@@ -18,6 +18,24 @@ struct AttnShape {
 // dt: 0 f32, 1 f16, 2 bf16 (the fa2_dtype values).
 hipError_t launch_fwd(int dt, const void *q, const void *k, const void *v, void *o, float *lse,
                       const AttnShape &s, hipStream_t stream);
+
+// Key-split forward plan: nsplit key ranges of split_len rows (the last may
+// be shorter), workgroups of `waves` wavefronts (32 query rows each).
+// nsplit == 1 runs the plain forward and needs no workspace.
+struct SplitPlan {
+    int nsplit;
+    int split_len;
+    int waves;
+    int64_t ws_bytes;  // float32 partial outputs and log2-sum-exps
+};
+// Key ranges start on multiples of this many rows (the forward's key tile).
+constexpr int kSplitKeyAlign = 64;
+// Host-only (no HIP call). requested <= 0 picks the split count from the
+// sizes: enough workgroups for one per CU of a 256-CU device, ranges of at
+// least 256 keys.
+SplitPlan plan_splitkv(int64_t bh, int64_t n_q, int64_t n_k, int head_dim, int requested);
+hipError_t launch_fwd_splitkv(int dt, const void *q, const void *k, const void *v, void *o, float *lse, float *ws,
+                              const AttnShape &s, const SplitPlan &sp, hipStream_t stream);
 hipError_t launch_bwd_delta(int dt, const void *o, const void *d_o, float *delta, int64_t rows,
                             int head_dim, hipStream_t stream);
 hipError_t launch_bwd_dq(int dt, const void *q, const void *k, const void *v, const void *d_o,

@@ -99,7 +99,6 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     constexpr int DV = 2 * KD;         // value width (V_lo | V_hi)
     constexpr int VEC = 8;             // elements per 16-byte vector
     constexpr int TS = KD / 16;        // contraction steps over channels
-    constexpr int NKB = BC / 32;
     constexpr int NDB = DV / 32;
     // LDS strides (elements). Transposing reads serve 4 rows x 64 bytes per
     // cycle: Q^T rows (BR queries) and K^T rows (BC keys) start 64 bytes apart

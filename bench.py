@@ -12,8 +12,10 @@ Legs measured in the same run (not part of `value`): the forward alone at
 that shape, cross-attention (BH 1024, Nq 1024, Nk 8192, D 64, K x 3), the
 backward-config step (BH 256, N 2048, D 128), the C2PSA block (pack,
 attention twice, merge, and the fused kernel) warm and with L2/MALL flushed
-before each call, and a reference bf16 GEMM (random and constant operands)
-that shows the chip's practical dense-MFMA ceiling on random data.
+before each call, a decoding shape (32 heads, 1 query row, 32768 keys,
+D 128) through the key-split forward and the plain forward, and a reference
+bf16 GEMM (random and constant operands) that shows the chip's practical
+dense-MFMA ceiling on random data.
 
 The CPU baseline times the fp64 oracle on a bounded sample of the same
 workload (a few heads at full sequence length) on the host cores.
@@ -48,7 +50,7 @@ def _parse():
     ap.add_argument("--no-legs", action="store_true", help="skip the other-shape legs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0, help="oracle sample heads (0: one per thread)")
-    ap.add_argument("--only", choices=["main", "c3_fwd", "c4", "c5", "c2", "gemm_ref"], default=None,
+    ap.add_argument("--only", choices=["main", "c3_fwd", "c4", "c5", "c2", "decode", "gemm_ref"], default=None,
                     help="run just the main step or just one leg (for profiling one workload); prints no JSON "
                          "line unless it is the main step")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -283,9 +285,36 @@ def _legs(torch, fa2, workloads, dev, only=None):
         _leg_c5(torch, fa2, workloads, dev, legs)
     if only in (None, "c2"):
         _leg_c2(torch, fa2, workloads, dev, legs)
+    if only in (None, "decode"):
+        _leg_decode(torch, fa2, workloads, dev, legs)
     if only in (None, "gemm_ref"):
         _leg_gemm_ref(torch, dev, legs)
     return legs
+
+
+def _leg_decode(torch, fa2, workloads, dev, legs):
+    """Decoding shape (32 heads, 1 query row, 32768 keys, D 128, bf16): the
+    key-split forward against the plain forward. HBM-bound: the algorithmic
+    bytes are Q, K, V, O and LSE once; K and V (537 MB) exceed the MALL, so
+    back-to-back calls stream them from HBM."""
+    w = workloads.DECODE
+    x = workloads.attn_inputs(w, device=dev)
+    o = torch.empty_like(x["q"])
+    lse = torch.empty((w.bh, w.n_q), dtype=torch.float32, device=dev)
+    splits, nbytes = fa2.fa2_fwd_splitkv_plan(w.torch_dtype, w.bh, w.n_q, w.n_k, w.head_dim, 0)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    es = 2
+    algo = w.bh * (2 * w.n_q * w.head_dim * es + 2 * w.n_k * w.head_dim * es + 4 * w.n_q)
+    ms_split = _time_fn(torch, lambda: fa2.fa2_fwd_splitkv(x["q"], x["k"], x["v"], w.scale, 0, ws, o, lse), 20)
+    ms_plain = _time_fn(torch, lambda: fa2.fa2_fwd(x["q"], x["k"], x["v"], w.scale, o, lse), 20)
+    gbs = algo / (ms_split * 1e-3) / 1e9
+    legs["decode"] = {"shape": [w.bh, w.n_q, w.n_k, w.head_dim], "splits": splits,
+                      "splitkv_us": round(ms_split * 1e3, 2), "fa2_fwd_us": round(ms_plain * 1e3, 2),
+                      "algorithmic_mb": round(algo / 1e6, 1), "splitkv_gbs": round(gbs, 1),
+                      "splitkv_frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    del x, o, lse, ws
+    torch.cuda.empty_cache()
+    print(f"[bench] leg decode {legs['decode']}", file=sys.stderr, flush=True)
 
 
 def _leg_gemm_ref(torch, dev, legs):

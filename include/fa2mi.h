@@ -2,11 +2,12 @@
  * fa2mi - exact FlashAttention-2 style attention for AMD Instinct MI355X
  * (gfx950), plus the PSA pack/merge rearrangements around it.
  *
- * C ABI. Every pointer argument is a DEVICE pointer owned by the caller; the
- * library never allocates, frees or keeps device memory and holds no state
- * between calls. Every call only validates its arguments and enqueues one
- * kernel on `stream` (a hipStream_t; NULL means the default stream), then
- * returns: results are ready once the caller synchronises that stream.
+ * C ABI. Every pointer argument is a DEVICE pointer owned by the caller
+ * unless stated otherwise; the library never allocates, frees or keeps device
+ * memory and holds no state between calls. Every call only validates its
+ * arguments and enqueues its kernel(s) on `stream` (a hipStream_t; NULL means
+ * the default stream), then returns: results are ready once the caller
+ * synchronises that stream.
  *
  * Layout (vision-rs flash_attn2.rs, module doc): attention tensors are flat
  * [BH, N, HEAD_DIM] row-major and contiguous, BH = batch * heads; the caller
@@ -78,6 +79,42 @@ const char *fa2_last_error(void);
 fa2_status fa2_fwd(fa2_dtype dt, const void *q, const void *k, const void *v, void *o, float *lse,
                    int64_t bh, int64_t n_q, int64_t n_k, int32_t head_dim, float scale,
                    void *stream);
+
+/*
+ * Key-split forward ("flash-decoding"): the same O and lse as fa2_fwd, for
+ * shapes with few query rows per head (decoding, short prompts against a
+ * long cache), where one workgroup per head and query block would leave most
+ * of the device idle. The key rows of each head are cut into consecutive
+ * ranges; pass 1 runs the forward's online-softmax recurrence (vision-rs
+ * flash_attn2.rs, "Forward") over each range separately, pass 2 merges the
+ * ranges by the log-sum-exp rule: with L_s = log sum_{j in range s} e^{s_ij}
+ * and O_s the range's softmax output,
+ *   lse = log sum_s e^{L_s},   O = sum_s e^{L_s - lse} O_s,
+ * which equals the single-range result exactly up to rounding (the same
+ * merge joins sequence shards across devices).
+ *
+ * fa2_fwd_splitkv_plan reports, for num_splits (0: chosen from the sizes,
+ * >0: requested; clamped to one range per 64 keys), the number of ranges
+ * used (*splits_used) and the workspace the call needs in bytes
+ * (*workspace_bytes = splits * bh * n_q * (head_dim + 1) * 4, or 0 when one
+ * range is used). Host-only; splits_used and workspace_bytes are host
+ * pointers; enqueues nothing.
+ *
+ * fa2_fwd_splitkv: arguments as fa2_fwd, plus `workspace`, a caller-owned
+ * device buffer of `workspace_bytes` bytes (16-byte aligned; may be NULL
+ * when the plan needs none), and num_splits as above. The workspace holds
+ * float32 partial results between the two passes; its contents on return
+ * are unspecified, and two calls in flight must not share one. Enqueues two
+ * kernels (one when a single range is used, which is fa2_fwd itself).
+ * FA2_ERR_INVALID_ARG also for num_splits < 0 and for a workspace smaller
+ * than the plan's size.
+ */
+fa2_status fa2_fwd_splitkv_plan(fa2_dtype dt, int64_t bh, int64_t n_q, int64_t n_k, int32_t head_dim,
+                                int32_t num_splits, int32_t *splits_used, int64_t *workspace_bytes);
+fa2_status fa2_fwd_splitkv(fa2_dtype dt, const void *q, const void *k, const void *v, void *o, float *lse,
+                           void *workspace, int64_t workspace_bytes,
+                           int64_t bh, int64_t n_q, int64_t n_k, int32_t head_dim, float scale,
+                           int32_t num_splits, void *stream);
 
 /*
  * Backward pre-pass (vision-rs flash_attn2.rs, "Backward - dQ": the per-row

@@ -99,6 +99,74 @@ def test_bwd_and_psa_reject_invalid_arguments():
     assert lib.psa_extract_v_backward(2, A, A, 16, 4, 32, -1, 20, None) == INVALID
 
 
+def _plan(dt, bh, n_q, n_k, d, splits):
+    lib = fa2.load()
+    used, nbytes = ctypes.c_int32(-7), ctypes.c_int64(-7)
+    st = lib.fa2_fwd_splitkv_plan(dt, bh, n_q, n_k, d, splits, ctypes.addressof(used), ctypes.addressof(nbytes))
+    return st, used.value, nbytes.value
+
+
+@pytest.mark.parametrize("bh,n_q,n_k,d,req", [
+    (32, 1, 32768, 128, 0), (32, 1, 32768, 128, 5), (3, 5, 1000, 64, 0), (2, 70, 333, 32, 0),
+    (1, 130, 5000, 128, 1000), (8, 1, 100, 128, 0), (512, 4096, 4096, 128, 0), (1, 1, 65, 32, 7),
+    (1, 1, 1, 64, 4), (7, 300, 9000, 64, 0),
+])
+def test_splitkv_plan(bh, n_q, n_k, d, req):
+    """The plan is host-only: split count and workspace size follow the
+    documented rule (ranges of a multiple of 64 keys covering n_k with no
+    empty range; one float32 output row plus one log-sum-exp per range and
+    query row; no workspace for a single range)."""
+    st, used, nbytes = _plan(2, bh, n_q, n_k, d, req)
+    assert st == OK
+    tiles = -(-n_k // 64)
+    assert 1 <= used <= tiles
+    if req > 0:
+        want = min(req, tiles)
+        length = -(-(-(-n_k // want)) // 64) * 64
+        assert used == -(-n_k // length)
+    length = -(-(-(-n_k // used)) // 64) * 64
+    assert (used - 1) * length < n_k <= used * length    # every range non-empty
+    assert nbytes == (0 if used == 1 else used * bh * n_q * (d + 1) * 4)
+
+
+def test_splitkv_plan_auto_fills_the_device():
+    # one query row, 32 heads, 32768 keys: 32 workgroups without the split
+    st, used, _ = _plan(2, 32, 1, 32768, 128, 0)
+    assert st == OK and used * 32 >= 256 and 32768 / used >= 256
+    # already one workgroup per CU or more: no split
+    assert _plan(2, 512, 4096, 4096, 128, 0)[1] == 1
+    # short key lengths are not cut below 256 keys per range
+    assert _plan(2, 1, 1, 600, 128, 0)[1] == 3
+
+
+def test_splitkv_rejects_invalid_arguments():
+    lib = fa2.load()
+    assert _plan(2, 32, 1, 4096, 128, -1)[0] == INVALID
+    assert _plan(2, 32, 1, 4096, 96, 0)[0] == UNSUPPORTED
+    assert _plan(2, 0, 1, 4096, 128, 0)[0] == INVALID
+    assert _plan(6, 1, 1, 4096, 128, 0)[0] == INVALID
+    assert lib.fa2_fwd_splitkv_plan(2, 32, 1, 4096, 128, 0, None, None) == INVALID
+    assert b"fa2_fwd_splitkv_plan" in lib.fa2_last_error()
+    _, used, need = _plan(2, 32, 1, 32768, 128, 0)
+    assert used > 1
+
+    def call(ws=A, nbytes=need, splits=0, **kw):
+        a = dict(dt=2, q=A, k=A, v=A, o=A, lse=A, bh=32, n_q=1, n_k=32768, d=128, scale=0.1)
+        a.update(kw)
+        return lib.fa2_fwd_splitkv(a["dt"], a["q"], a["k"], a["v"], a["o"], a["lse"], ws, nbytes, a["bh"],
+                                   a["n_q"], a["n_k"], a["d"], a["scale"], splits, None)
+
+    assert call(nbytes=need - 1) == INVALID                  # workspace too small
+    assert b"workspace_bytes" in lib.fa2_last_error()
+    assert call(ws=None) == INVALID
+    assert call(ws=MIS) == INVALID
+    assert call(splits=-2) == INVALID
+    assert call(q=None) == INVALID
+    assert call(d=16) == UNSUPPORTED
+    assert call(scale=0.0) == INVALID
+    assert b"fa2_fwd_splitkv" in lib.fa2_last_error()
+
+
 def test_binding_refuses_host_tensors():
     q = torch.zeros(1, 8, 32, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU tensor"):

@@ -153,6 +153,74 @@ def test_fwd_c4_cross_attention_sampled():
 
 
 # ---------------------------------------------------------------------------
+# Key-split forward (few query rows per head)
+
+SPLIT_SHAPES = [(4, 1, 3000), (3, 5, 1000), (2, 70, 333), (1, 130, 700), (2, 64, 64), (1, 1, 65), (2, 257, 129)]
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("splits", [0, 3])
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_fwd_splitkv_small(dt, d, splits, shape):
+    bh, nq, nk = shape
+    used, nbytes = fa2.fa2_fwd_splitkv_plan(DTYPES[dt], bh, nq, nk, d, splits)
+    case = f"splitkv {dt} d={d} bh={bh} nq={nq} nk={nk} splits={splits}->{used}"
+    print(case, flush=True)
+    x = _inputs(dt, bh, nq, nk, d, seed=300 + nq + nk + d)
+    scale = 1 / math.sqrt(d)
+    # workspace and outputs with NaN canaries past their ends
+    ws = torch.full((nbytes + 4096,), 0xFF, dtype=torch.uint8, device=DEV)
+    obuf = torch.full((bh * nq * d + 256,), float("nan"), dtype=x["q"].dtype, device=DEV)
+    lbuf = torch.full((bh * nq + 256,), float("nan"), dtype=torch.float32, device=DEV)
+    o = obuf[: bh * nq * d].view(bh, nq, d)
+    lse = lbuf[: bh * nq].view(bh, nq)
+    fa2.fa2_fwd_splitkv(x["q"], x["k"], x["v"], scale, splits, ws[:max(nbytes, 16)], o, lse)
+    torch.cuda.synchronize()
+    assert torch.isnan(obuf[bh * nq * d:]).all() and torch.isnan(lbuf[bh * nq:]).all()
+    assert (ws[max(nbytes, 16):] == 0xFF).all()
+    o_ref, lse_ref = oracle.attention_fwd(x["q"], x["k"], x["v"], scale)
+    tol = TOL[DTYPES[dt]]
+    _err("O", _np(o), o_ref, tol, case)
+    _err("LSE", _np(lse), lse_ref, tol, case)
+
+
+def test_fwd_splitkv_decode_full():
+    """Decoding shape at full size: 32 heads, one query row, 32768 keys,
+    head_dim 128, bfloat16; every output against the oracle, and the split
+    count the plan picks actually spreads the keys."""
+    bh, nq, nk, d = 32, 1, 32768, 128
+    used, _ = fa2.fa2_fwd_splitkv_plan(torch.bfloat16, bh, nq, nk, d, 0)
+    assert used >= 8
+    x = _inputs("bf16", bh, nq, nk, d, seed=31)
+    o, lse = fa2.fa2_fwd_splitkv(x["q"], x["k"], x["v"])
+    o1, lse1 = fa2.fa2_fwd(x["q"], x["k"], x["v"])
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_fwd(x["q"], x["k"], x["v"], 1 / math.sqrt(d))
+    case = f"decode bh={bh} nk={nk} splits={used}"
+    _err("O", _np(o), o_ref, 2e-2, case)
+    _err("LSE", _np(lse), lse_ref, 2e-2, case)
+    _err("O (fa2_fwd)", _np(o1), o_ref, 2e-2, case)
+
+
+def test_fwd_splitkv_workspace_reuse():
+    """Two calls in a row on one workspace, the second smaller: the second
+    result does not depend on what the first left behind."""
+    x = _inputs("bf16", 8, 3, 5000, 64, seed=41)
+    y = _inputs("bf16", 2, 1, 700, 64, seed=42)
+    ws = torch.empty(fa2.fa2_fwd_splitkv_plan(torch.bfloat16, 8, 3, 5000, 64, 0)[1], dtype=torch.uint8,
+                     device=DEV)
+    fa2.fa2_fwd_splitkv(x["q"], x["k"], x["v"], workspace=ws)
+    o, lse = fa2.fa2_fwd_splitkv(y["q"], y["k"], y["v"], workspace=ws)
+    o2, lse2 = fa2.fa2_fwd_splitkv(y["q"], y["k"], y["v"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    o_ref, lse_ref = oracle.attention_fwd(y["q"], y["k"], y["v"], 1 / 8.0)
+    _err("O", _np(o), o_ref, 2e-2, "reuse")
+    _err("LSE", _np(lse), lse_ref, 2e-2, "reuse")
+
+
+# ---------------------------------------------------------------------------
 # PSA
 
 

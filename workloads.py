@@ -123,7 +123,12 @@ C4 = AttnWorkload("c4_xattn_bf16", bh=1024, n_q=1024, n_k=8192, head_dim=64, dty
 C5 = AttnWorkload("c5_bwd_bf16", bh=256, n_q=2048, n_k=2048, head_dim=128, dtype="bf16", seed=5,
                   backward=True, note="backward from the forward's O and fp32 LSE")
 
-ATTN_WORKLOADS = {w.name: w for w in (C1, C3, C4, C5)}
+# Not one of the five configurations: a decoding-shaped forward (one query
+# row per head against a long key cache) for the key-split forward.
+DECODE = AttnWorkload("decode_bf16", bh=32, n_q=1, n_k=32768, head_dim=128, dtype="bf16", seed=6,
+                      note="decoding: 32 heads, 1 query row, 32768 keys")
+
+ATTN_WORKLOADS = {w.name: w for w in (C1, C3, C4, C5, DECODE)}
 PSA_WORKLOADS = {C2.name: C2}
 
 
