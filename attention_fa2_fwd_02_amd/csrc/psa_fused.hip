@@ -245,11 +245,12 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 
 // Small feature maps (the usual C2PSA case: h*w of a few hundred pixels).
 // One workgroup per (head, 128 queries), 8 waves = 4 query sub-blocks of 32
-// x 2 key halves of NB blocks of 32 keys each. The head's whole K^T and V^T
-// (zero past h*w) and the Q^T block are fetched into LDS in one burst; each
-// wave keeps the scores of its key half in registers, so its softmax needs
-// one exact row max and one exp2 pass, no online rescaling, and every loop
-// has a fixed trip count (keys past h*w are masked, not skipped). The two
+// x 2 key halves of at most NB blocks of 32 keys each (the map's
+// ceil(h*w / 32) blocks split evenly; a ragged last block is masked). The
+// head's whole K^T and V^T (zero past h*w) and the Q^T block are fetched into
+// LDS in one burst; each wave keeps the scores of its key half in registers,
+// so its softmax needs one exact row max and one exp2 pass, no online
+// rescaling; its block loops have wave-uniform trip counts. The two
 // key halves of a query sub-block are merged through LDS with the
 // online-softmax combination (max, rescaled sums), each wave finishing half
 // of the value channels and storing them straight to the pixel rows.
@@ -362,9 +363,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     __syncthreads();
 
-    // this wave: queries q0 + 32 qs + [0, 32), key blocks ks*NB + [0, NB)
-    const int kb0 = ks * NB;
-    const bool active = q0 + 32 * qs < hw;
+    // this wave: queries q0 + 32 qs + [0, 32), key blocks kb0 + [0, nb): the
+    // map's ceil(hw / 32) key blocks split evenly between the two halves
+    // (nb <= NB since hw <= 64 NB); blocks past nb are not computed
+    const int nblk = (hw + 31) / 32, nb_lo = (nblk + 1) / 2;
+    const int kb0 = ks ? nb_lo : 0;
+    const int nb = ks ? nblk - nb_lo : nb_lo;
+    const bool active = q0 + 32 * qs < hw && nb > 0;
     f32x16 acc[NDB];
 #pragma unroll
     for (int i = 0; i < NDB; ++i) acc[i] = zero16();
@@ -376,6 +381,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int t = 0; t < TS; ++t) qf[t] = ld_vt_frag_tr<DT>(Qt, LDQ, 16 * t, 32 * qs, lane);
 #pragma unroll
         for (int kb = 0; kb < NB; ++kb) {
+            if (kb >= nb) break;
             s[kb] = zero16();
 #pragma unroll
             for (int t = 0; t < TS; ++t)
@@ -386,6 +392,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < NB; ++kb) {
+            if (kb >= nb) break;
             if (32 * (kb0 + kb + 1) > hw) {
                 const int limit = hw - 32 * (kb0 + kb) - 4 * h;  // first invalid crow - 4h
 #pragma unroll
@@ -404,6 +411,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const float neg_m = m == -INFINITY ? 0.f : -m;
 #pragma unroll
         for (int kb = 0; kb < NB; ++kb) {
+            if (kb >= nb) break;
 #pragma unroll
             for (int c = 0; c < 16; ++c) s[kb][c] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][c], scale_log2, neg_m));
 #pragma unroll
