@@ -10,11 +10,12 @@ every function raises if the library is missing or the tensors are not on a
 GPU.
 
 Entry points (same names as the C ABI):
-  fa2_fwd, fa2_fwd_splitkv_plan, fa2_fwd_splitkv, fa2_bwd_delta, fa2_bwd_dq, fa2_bwd_dkdv, psa_pack_qkv, psa_merge_attn,
+  fa2_fwd, fa2_fwd_splitkv_plan, fa2_fwd_splitkv, fa2_pad_cols, fa2_bwd_delta, fa2_bwd_dq, fa2_bwd_dkdv, psa_pack_qkv, psa_merge_attn,
   psa_attn_fused, psa_merge_attn_backward, psa_pack_qkv_backward,
   psa_extract_v_nchw, psa_extract_v_backward
 Compositions of them:
-  attention_fwd (= fa2_fwd), attention_bwd (delta -> dkdv -> dq),
+  attention_fwd (fa2_fwd; other head dims up to 128 through zero padding with
+  fa2_pad_cols), attention_bwd (delta -> dkdv -> dq, padded likewise),
   psa_block (pack -> fa2_fwd on V_lo -> fa2_fwd on V_hi -> merge),
   psa_block_backward (merge backward -> the attention backward of both calls
   -> pack backward, adding the two calls' dQ and dK)
@@ -30,7 +31,7 @@ from . import _lib
 from ._lib import FA2_BF16, FA2_F16, FA2_F32, Fa2Error, library_path, load  # noqa: F401
 
 __all__ = [
-    "fa2_fwd", "fa2_fwd_splitkv_plan", "fa2_fwd_splitkv", "fa2_bwd_delta", "fa2_bwd_dq", "fa2_bwd_dkdv", "psa_pack_qkv", "psa_merge_attn", "psa_attn_fused",
+    "fa2_fwd", "fa2_fwd_splitkv_plan", "fa2_fwd_splitkv", "fa2_pad_cols", "fa2_bwd_delta", "fa2_bwd_dq", "fa2_bwd_dkdv", "psa_pack_qkv", "psa_merge_attn", "psa_attn_fused",
     "psa_merge_attn_backward", "psa_pack_qkv_backward", "psa_extract_v_nchw", "psa_extract_v_backward",
     "attention_fwd", "attention_bwd", "psa_block", "psa_block_backward", "Fa2Error", "load", "library_path",
 ]
@@ -184,13 +185,50 @@ def fa2_bwd_dkdv(q, k, v, do, lse, delta, scale=None, dk=None, dv=None):
     return dk, dv
 
 
+NATIVE_HEAD_DIMS = (32, 64, 128)
+
+
+def fa2_pad_cols(x, d_out, out=None):
+    """x [..., d] -> [..., d_out]: the first min(d, d_out) columns of every
+    row, zeros after them (pads when d_out > d, crops when d_out < d)."""
+    _check("x", x)
+    d = x.shape[-1]
+    shape = tuple(x.shape[:-1]) + (d_out,)
+    if out is None:
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    _check("out", out, x.dtype, shape, x.device)
+    rows = x.numel() // d
+    _lib.call("fa2_pad_cols", _dtype_code(x), x.data_ptr(), out.data_ptr(), rows, d, d_out, _stream(x.device))
+    return out
+
+
+def _padded_dim(d: int) -> int:
+    for n in NATIVE_HEAD_DIMS:
+        if d <= n:
+            return n
+    raise ValueError(f"head_dim {d} > {NATIVE_HEAD_DIMS[-1]} is not supported")
+
+
 def attention_fwd(q, k, v, scale=None):
-    """(o, lse) of softmax(scale q k^T) v."""
-    return fa2_fwd(q, k, v, scale)
+    """(o, lse) of softmax(scale q k^T) v. Head dims other than 32, 64 and 128
+    (up to 128) run on zero-padded copies; scale defaults to 1/sqrt of the
+    original head dim."""
+    d = q.shape[-1]
+    if d in NATIVE_HEAD_DIMS:
+        return fa2_fwd(q, k, v, scale)
+    dp = _padded_dim(d)
+    o, lse = fa2_fwd(fa2_pad_cols(q, dp), fa2_pad_cols(k, dp), fa2_pad_cols(v, dp), _scale(scale, d))
+    return fa2_pad_cols(o, d), lse
 
 
 def attention_bwd(q, k, v, o, do, lse, scale=None):
-    """(dq, dk, dv) given the forward's o and lse and the output gradient do."""
+    """(dq, dk, dv) given the forward's o and lse and the output gradient do
+    (other head dims up to 128 through zero padding, as attention_fwd)."""
+    d = q.shape[-1]
+    if d not in NATIVE_HEAD_DIMS:
+        dp = _padded_dim(d)
+        dq, dk, dv = attention_bwd(*(fa2_pad_cols(t, dp) for t in (q, k, v, o, do)), lse, _scale(scale, d))
+        return fa2_pad_cols(dq, d), fa2_pad_cols(dk, d), fa2_pad_cols(dv, d)
     delta = fa2_bwd_delta(o, do)
     dk, dv = fa2_bwd_dkdv(q, k, v, do, lse, delta, scale)
     dq = fa2_bwd_dq(q, k, v, do, lse, delta, scale)

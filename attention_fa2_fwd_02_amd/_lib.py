@@ -27,6 +27,7 @@ SIGNATURES = {
     "fa2_bwd_delta": [_int, _p, _p, _p, _i64, _i64, _i32, _p],
     "fa2_bwd_dq": [_int, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i32, _f32, _p],
     "fa2_bwd_dkdv": [_int, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i32, _f32, _p],
+    "fa2_pad_cols": [_int, _p, _p, _i64, _i32, _i32, _p],
     "psa_pack_qkv": [_int, _p, _p, _i32, _i32, _i32, _i32, _i32, _p],
     "psa_merge_attn": [_int, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _p],
     "psa_attn_fused": [_int, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _p],

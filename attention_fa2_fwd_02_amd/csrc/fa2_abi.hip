@@ -224,6 +224,20 @@ fa2_status fa2_bwd_dkdv(fa2_dtype dt, const void *q, const void *k, const void *
     return launched(fn, fa2mi::launch_bwd_dkdv((int)dt, q, k, v, d_o, lse, delta, dk, dv, s, (hipStream_t)stream));
 }
 
+fa2_status fa2_pad_cols(fa2_dtype dt, const void *src, void *dst, int64_t rows, int32_t d_src, int32_t d_dst,
+                        void *stream) {
+    static const char fn[] = "fa2_pad_cols";
+    if (!good_dtype(dt)) return fail(FA2_ERR_INVALID_ARG, fn, "unknown dtype");
+    if (rows <= 0 || d_src <= 0 || d_dst <= 0) return fail(FA2_ERR_INVALID_ARG, fn, "rows, d_src and d_dst must be > 0");
+    if ((rows + fa2mi::kPadColsRowsPerBlock - 1) / fa2mi::kPadColsRowsPerBlock > INT_MAX)
+        return fail(FA2_ERR_INVALID_ARG, fn, "grid exceeds 2^31 - 1 workgroups");
+    if ((int64_t)fa2mi::kPadColsRowsPerBlock * (d_src > d_dst ? d_src : d_dst) > INT_MAX)
+        return fail(FA2_ERR_INVALID_ARG, fn, "row width too large");
+    REQUIRE_PTR(fn, src);
+    REQUIRE_PTR(fn, dst);
+    return launched(fn, fa2mi::launch_pad_cols((int)dt, src, dst, rows, d_src, d_dst, (hipStream_t)stream));
+}
+
 fa2_status psa_pack_qkv(fa2_dtype dt, const void *qkv, void *packed, int32_t batch, int32_t num_heads,
                         int32_t key_dim, int32_t h, int32_t w, void *stream) {
     static const char fn[] = "psa_pack_qkv";

@@ -45,6 +45,13 @@ hipError_t launch_bwd_dkdv(int dt, const void *q, const void *k, const void *v, 
                            const float *lse, const float *delta, void *dk, void *dv,
                            const AttnShape &s, hipStream_t stream);
 
+// Row-major [rows, d_src] -> [rows, d_dst]: copy the first min(d_src, d_dst)
+// columns, zero the rest (d_dst > d_src pads, d_dst < d_src crops).
+hipError_t launch_pad_cols(int dt, const void *src, void *dst, int64_t rows, int d_src, int d_dst,
+                           hipStream_t stream);
+// Rows moved per workgroup of the column copy (the ABI bounds its grid).
+constexpr int kPadColsRowsPerBlock = 16;
+
 struct PsaShape {
     int batch;
     int num_heads;

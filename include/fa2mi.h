@@ -20,8 +20,9 @@
  * is always float32; outputs are rounded to `dt` with round-to-nearest-even.
  * lse and delta are always float32. LSE is in natural-log units.
  *
- * Supported: head_dim in {32, 64, 128}; non-causal attention without mask,
- * dropout or bias (the pages describe none).
+ * Supported: head_dim in {32, 64, 128} (other head dims up to 128 through
+ * fa2_pad_cols, below); non-causal attention without mask, dropout or bias
+ * (the pages describe none).
  *
  * Errors (checked on the host before anything is enqueued; nothing is enqueued
  * when a call fails):
@@ -148,6 +149,22 @@ fa2_status fa2_bwd_dq(fa2_dtype dt, const void *q, const void *k, const void *v,
 fa2_status fa2_bwd_dkdv(fa2_dtype dt, const void *q, const void *k, const void *v, const void *d_o,
                         const float *lse, const float *delta, void *dk, void *dv,
                         int64_t bh, int64_t n_q, int64_t n_k, int32_t head_dim, float scale,
+                        void *stream);
+
+/*
+ * Column pad / crop for head dims the attention kernels do not take
+ * (vyre-libs flash_attention_2.rs tests run head dims 4, 7, 8 and 16):
+ *   dst[r][c] = src[r][c]  for c < min(d_src, d_dst),   0 for d_src <= c < d_dst,
+ * over row-major src [rows, d_src] and dst [rows, d_dst] (dt elements; bit
+ * copy). Widening q, k and v of any head_dim <= 128 with zero columns to the
+ * next supported size (32, 64, 128) leaves every score q . k unchanged and
+ * only adds output columns equal to zero, so fa2_fwd / fa2_bwd_* on the padded
+ * copies (with the ORIGINAL head_dim's softmax scale) followed by a crop back
+ * to d_src columns give O, lse, dq, dk and dv of the original problem. The
+ * Python binding's attention_fwd / attention_bwd do exactly that.
+ * FA2_ERR_INVALID_ARG for sizes <= 0, NULL or misaligned pointers.
+ */
+fa2_status fa2_pad_cols(fa2_dtype dt, const void *src, void *dst, int64_t rows, int32_t d_src, int32_t d_dst,
                         void *stream);
 
 /*

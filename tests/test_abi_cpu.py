@@ -167,6 +167,25 @@ def test_splitkv_rejects_invalid_arguments():
     assert b"fa2_fwd_splitkv" in lib.fa2_last_error()
 
 
+def test_pad_cols_rejects_invalid_arguments():
+    lib = fa2.load()
+    assert lib.fa2_pad_cols(1, A, A, 0, 7, 32, None) == INVALID
+    assert lib.fa2_pad_cols(1, A, A, 10, 0, 32, None) == INVALID
+    assert lib.fa2_pad_cols(1, A, A, 10, 7, -1, None) == INVALID
+    assert lib.fa2_pad_cols(4, A, A, 10, 7, 32, None) == INVALID
+    assert lib.fa2_pad_cols(2, None, A, 10, 7, 32, None) == INVALID
+    assert lib.fa2_pad_cols(2, A, MIS, 10, 7, 32, None) == INVALID
+    assert lib.fa2_pad_cols(2, A, A, 1 << 40, 7, 32, None) == INVALID   # grid
+    assert b"fa2_pad_cols" in lib.fa2_last_error()
+
+
+def test_binding_pads_only_unsupported_head_dims():
+    assert [fa2._padded_dim(d) for d in (1, 4, 7, 8, 16, 32, 33, 64, 100, 128)] == \
+        [32, 32, 32, 32, 32, 32, 64, 64, 128, 128]
+    with pytest.raises(ValueError, match="not supported"):
+        fa2._padded_dim(129)
+
+
 def test_binding_refuses_host_tensors():
     q = torch.zeros(1, 8, 32, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU tensor"):

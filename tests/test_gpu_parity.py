@@ -153,6 +153,57 @@ def test_fwd_c4_cross_attention_sampled():
 
 
 # ---------------------------------------------------------------------------
+# Head dims outside {32, 64, 128}: zero padding through fa2_pad_cols
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_pad_cols_bitexact(dt):
+    """Padding and cropping are bit copies: the padded tensor is torch's
+    zero-padded tensor, and cropping it back returns the input."""
+    g = torch.Generator(device="cpu").manual_seed(61)
+    x = torch.randn(3, 37, 7, generator=g).to(DTYPES[dt]).to(DEV)
+    for d_out in (7, 8, 32, 100, 128):
+        y = fa2.fa2_pad_cols(x, d_out)
+        back = fa2.fa2_pad_cols(y, 7)
+        torch.cuda.synchronize()
+        want = torch.nn.functional.pad(x.cpu(), (0, max(0, d_out - 7)))[..., :d_out]
+        assert torch.equal(y.cpu(), want), d_out
+        assert torch.equal(back.cpu(), x.cpu()), d_out
+    # crop below the input width
+    z = fa2.fa2_pad_cols(x, 3)
+    torch.cuda.synchronize()
+    assert torch.equal(z.cpu(), x.cpu()[..., :3])
+
+
+ANY_DIM_SHAPES = [(2, 64, 64), (1, 129, 70), (2, 1, 200)]
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("d", [4, 7, 8, 16, 40, 100])
+@pytest.mark.parametrize("shape", ANY_DIM_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_fwd_bwd_any_head_dim(dt, d, shape):
+    """Head dims the kernels are not built for (the vyre-libs tests use 4, 7,
+    8 and 16) through zero padding to 32 / 64 / 128: forward and backward
+    against the oracle at the original head dim and scale."""
+    bh, nq, nk = shape
+    case = f"any-dim {dt} d={d} bh={bh} nq={nq} nk={nk}"
+    print(case, flush=True)
+    x = _inputs(dt, bh, nq, nk, d, seed=400 + nq + nk + d, with_do=True)
+    scale = 1 / math.sqrt(d)
+    o, lse = fa2.attention_fwd(x["q"], x["k"], x["v"])
+    dq, dk, dv = fa2.attention_bwd(x["q"], x["k"], x["v"], o, x["do"], lse)
+    torch.cuda.synchronize()
+    assert o.shape == x["q"].shape and dk.shape == x["k"].shape
+    tol = TOL[DTYPES[dt]]
+    o_ref, lse_ref = oracle.attention_fwd(x["q"], x["k"], x["v"], scale)
+    _err("O", _np(o), o_ref, tol, case)
+    _err("LSE", _np(lse), lse_ref, tol, case)
+    ref = oracle.attention_bwd(x["q"], x["k"], x["v"], x["do"], scale)
+    for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        _err(name, _np(got), want, tol, case)
+
+
+# ---------------------------------------------------------------------------
 # Key-split forward (few query rows per head)
 
 SPLIT_SHAPES = [(4, 1, 3000), (3, 5, 1000), (2, 70, 333), (1, 130, 700), (2, 64, 64), (1, 1, 65), (2, 257, 129)]
