@@ -49,7 +49,7 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-legs", action="store_true", help="skip the other-shape legs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=0, help="oracle sample heads (0: one per thread)")
+    ap.add_argument("--cpu-heads", type=int, default=0, help="oracle sample heads (0: three per thread)")
     ap.add_argument("--only", choices=["main", "c3_fwd", "c4", "c5", "c2", "decode", "gemm_ref"], default=None,
                     help="run just the main step or just one leg (for profiling one workload); prints no JSON "
                          "line unless it is the main step")
@@ -448,7 +448,7 @@ def _cpu_baseline(w, heads_arg):
     import workloads
 
     threads = oracle.default_threads()
-    heads = heads_arg or threads
+    heads = heads_arg or 3 * threads  # three full-length heads per thread: ~10-20 s
     x = workloads.attn_inputs(w, device="cpu", bh=heads, with_do=True, seed=w.seed)
     print(f"[bench] cpu baseline: oracle fwd+bwd on {heads} heads, {threads} threads", file=sys.stderr, flush=True)
     q, k, v, do = (oracle._f64(x[n]) for n in ("q", "k", "v", "do"))
