@@ -203,6 +203,45 @@ def test_fwd_bwd_any_head_dim(dt, d, shape):
         _err(name, _np(got), want, tol, case)
 
 
+def test_vyre_trig_fixture_head_dim_16():
+    """The vyre-libs tiled-versus-reference test case (tests section of
+    flash_attention_2.rs): one head, 8 rows, head_dim 16, float32, inputs
+    given by sines and cosines of the flat element index, scale 1/sqrt(16).
+    Head_dim 16 runs padded to 32; forward and backward against the oracle
+    (bar 1e-4; the page's own bar between its two implementations is 1e-3)."""
+    n, d = 8, 16
+    i = torch.arange(n * d, dtype=torch.float64)
+    q = (torch.sin(0.13 * i) - 0.5).float().view(1, n, d)
+    k = (torch.cos(0.07 * i) + 0.25).float().view(1, n, d)
+    v = (2.0 * torch.sin(0.19 * i)).float().view(1, n, d)
+    do = torch.cos(0.11 * i).float().view(1, n, d)
+    o, lse = fa2.attention_fwd(q.to(DEV), k.to(DEV), v.to(DEV))
+    dq, dk, dv = fa2.attention_bwd(q.to(DEV), k.to(DEV), v.to(DEV), o, do.to(DEV), lse)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_fwd(q, k, v, 0.25)
+    _err("O", _np(o), o_ref, 1e-4, "vyre trig fixture")
+    _err("LSE", _np(lse), lse_ref, 1e-4, "vyre trig fixture")
+    ref = oracle.attention_bwd(q, k, v, do, 0.25)
+    for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        _err(name, _np(got), want, 1e-4, "vyre trig fixture")
+
+
+def test_vyre_constant_fixture_head_dim_7():
+    """The vyre-libs output-shape test case: 5 rows, head_dim 7, q = 1,
+    k = 0.5, v = 2 everywhere. All scores are equal, so O = v = 2 exactly and
+    lse = scale * 7 * 0.5 + ln 5 with scale = 1/sqrt(7)."""
+    n, d = 5, 7
+    q = torch.full((1, n, d), 1.0, device=DEV)
+    k = torch.full((1, n, d), 0.5, device=DEV)
+    v = torch.full((1, n, d), 2.0, device=DEV)
+    o, lse = fa2.attention_fwd(q, k, v)
+    torch.cuda.synchronize()
+    assert o.shape == (1, n, d)
+    assert torch.allclose(o.cpu(), torch.full((1, n, d), 2.0), rtol=0, atol=1e-6)
+    want = 3.5 / math.sqrt(7.0) + math.log(5.0)
+    assert torch.allclose(lse.cpu().double(), torch.full((1, n), want, dtype=torch.float64), atol=1e-5)
+
+
 # ---------------------------------------------------------------------------
 # Key-split forward (few query rows per head)
 
