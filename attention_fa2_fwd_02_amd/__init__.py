@@ -10,12 +10,14 @@ every function raises if the library is missing or the tensors are not on a
 GPU.
 
 Entry points (same names as the C ABI):
-  fa2_fwd, fa2_fwd_splitkv_plan, fa2_fwd_splitkv, fa2_pad_cols, fa2_bwd_delta, fa2_bwd_dq, fa2_bwd_dkdv, psa_pack_qkv, psa_merge_attn,
-  psa_attn_fused, psa_merge_attn_backward, psa_pack_qkv_backward,
+  fa2_fwd, fa2_fwd_splitkv_plan, fa2_fwd_splitkv, fa2_pad_cols, fa2_bwd_delta,
+  fa2_bwd_dq, fa2_bwd_dkdv, psa_pack_qkv, psa_merge_attn, psa_attn_fused,
+  psa_attn_fused_backward, psa_merge_attn_backward, psa_pack_qkv_backward,
   psa_extract_v_nchw, psa_extract_v_backward
 Compositions of them:
-  attention_fwd (fa2_fwd; other head dims up to 128 through zero padding with
-  fa2_pad_cols), attention_bwd (delta -> dkdv -> dq, padded likewise),
+  attention_fwd (fa2_fwd, or fa2_fwd_splitkv when its plan splits the keys;
+  other head dims up to 128 through zero padding with fa2_pad_cols),
+  attention_bwd (delta -> dkdv -> dq, padded likewise),
   psa_block (pack -> fa2_fwd on V_lo -> fa2_fwd on V_hi -> merge),
   psa_block_backward (merge backward -> the attention backward of both calls
   -> pack backward, adding the two calls' dQ and dK)
@@ -31,7 +33,8 @@ from . import _lib
 from ._lib import FA2_BF16, FA2_F16, FA2_F32, Fa2Error, library_path, load  # noqa: F401
 
 __all__ = [
-    "fa2_fwd", "fa2_fwd_splitkv_plan", "fa2_fwd_splitkv", "fa2_pad_cols", "fa2_bwd_delta", "fa2_bwd_dq", "fa2_bwd_dkdv", "psa_pack_qkv", "psa_merge_attn", "psa_attn_fused",
+    "fa2_fwd", "fa2_fwd_splitkv_plan", "fa2_fwd_splitkv", "fa2_pad_cols", "fa2_bwd_delta", "fa2_bwd_dq",
+    "fa2_bwd_dkdv", "psa_pack_qkv", "psa_merge_attn", "psa_attn_fused", "psa_attn_fused_backward",
     "psa_merge_attn_backward", "psa_pack_qkv_backward", "psa_extract_v_nchw", "psa_extract_v_backward",
     "attention_fwd", "attention_bwd", "psa_block", "psa_block_backward", "Fa2Error", "load", "library_path",
 ]
@@ -209,15 +212,27 @@ def _padded_dim(d: int) -> int:
     raise ValueError(f"head_dim {d} > {NATIVE_HEAD_DIMS[-1]} is not supported")
 
 
+def _fwd_auto(q, k, v, scale):
+    """fa2_fwd, or the key-split forward when the split plan uses more than
+    one key range (few query rows per head: the plain grid would leave most
+    CUs idle)."""
+    bh, n_q, d = q.shape
+    splits, _ = fa2_fwd_splitkv_plan(q.dtype, bh, n_q, k.shape[1], d, 0)
+    if splits > 1:
+        return fa2_fwd_splitkv(q, k, v, scale)
+    return fa2_fwd(q, k, v, scale)
+
+
 def attention_fwd(q, k, v, scale=None):
-    """(o, lse) of softmax(scale q k^T) v. Head dims other than 32, 64 and 128
-    (up to 128) run on zero-padded copies; scale defaults to 1/sqrt of the
-    original head dim."""
+    """(o, lse) of softmax(scale q k^T) v. Shapes with few query rows per head
+    take the key-split forward; head dims other than 32, 64 and 128 (up to
+    128) run on zero-padded copies; scale defaults to 1/sqrt of the original
+    head dim."""
     d = q.shape[-1]
     if d in NATIVE_HEAD_DIMS:
-        return fa2_fwd(q, k, v, scale)
+        return _fwd_auto(q, k, v, scale)
     dp = _padded_dim(d)
-    o, lse = fa2_fwd(fa2_pad_cols(q, dp), fa2_pad_cols(k, dp), fa2_pad_cols(v, dp), _scale(scale, d))
+    o, lse = _fwd_auto(fa2_pad_cols(q, dp), fa2_pad_cols(k, dp), fa2_pad_cols(v, dp), _scale(scale, d))
     return fa2_pad_cols(o, d), lse
 
 
@@ -305,6 +320,31 @@ def psa_attn_fused(qkv, num_heads: int, key_dim: int, out=None, lse=None):
     _lib.call("psa_attn_fused", _dtype_code(qkv), qkv.data_ptr(), out.data_ptr(), lse_ptr, b, num_heads, key_dim,
               h, w, _stream(qkv.device))
     return out
+
+
+def psa_attn_fused_backward(qkv, out, lse, d_out, num_heads: int, key_dim: int, d_qkv=None, delta=None):
+    """Gradient of the PSA attention block with respect to qkv, from qkv, the
+    block output `out` and its `lse` (psa_attn_fused with lse) and d_out.
+    Returns d_qkv [B, nh*4*kd, H, W] (key_dim 32, H*W <= 512; f16/bf16).
+    `delta` ([B*nh, H*W] float32) receives rowsum(out * d_out) per pixel."""
+    _check("qkv", qkv)
+    b, ch, h, w = qkv.shape
+    if ch != num_heads * 4 * key_dim:
+        raise ValueError(f"qkv has {ch} channels, expected num_heads*4*key_dim = {num_heads * 4 * key_dim}")
+    dev = qkv.device
+    oshape = (b, num_heads * 2 * key_dim, h, w)
+    _check("out", out, qkv.dtype, oshape, dev)
+    _check("d_out", d_out, qkv.dtype, oshape, dev)
+    _check("lse", lse, torch.float32, (b * num_heads, h * w), dev)
+    if d_qkv is None:
+        d_qkv = torch.empty_like(qkv)
+    _check("d_qkv", d_qkv, qkv.dtype, qkv.shape, dev)
+    if delta is None:
+        delta = torch.empty((b * num_heads, h * w), dtype=torch.float32, device=dev)
+    _check("delta", delta, torch.float32, (b * num_heads, h * w), dev)
+    _lib.call("psa_attn_fused_backward", _dtype_code(qkv), qkv.data_ptr(), out.data_ptr(), lse.data_ptr(),
+              d_out.data_ptr(), d_qkv.data_ptr(), delta.data_ptr(), b, num_heads, key_dim, h, w, _stream(dev))
+    return d_qkv
 
 
 def psa_merge_attn_backward(d_out, num_heads: int, key_dim: int, d_o_lo=None, d_o_hi=None):

@@ -31,6 +31,7 @@ SIGNATURES = {
     "psa_pack_qkv": [_int, _p, _p, _i32, _i32, _i32, _i32, _i32, _p],
     "psa_merge_attn": [_int, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _p],
     "psa_attn_fused": [_int, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _p],
+    "psa_attn_fused_backward": [_int, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _p],
     "psa_merge_attn_backward": [_int, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _p],
     "psa_pack_qkv_backward": [_int, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _p],
     "psa_extract_v_nchw": [_int, _p, _p, _i32, _i32, _i32, _i32, _i32, _p],

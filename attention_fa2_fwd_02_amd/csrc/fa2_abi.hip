@@ -324,4 +324,25 @@ fa2_status psa_attn_fused(fa2_dtype dt, const void *qkv, void *out, float *lse, 
     return launched(fn, fa2mi::launch_psa_fused((int)dt, qkv, out, lse, s, (hipStream_t)stream));
 }
 
+fa2_status psa_attn_fused_backward(fa2_dtype dt, const void *qkv, const void *out, const float *lse,
+                                   const void *d_out, void *d_qkv, float *delta, int32_t batch, int32_t num_heads,
+                                   int32_t key_dim, int32_t h, int32_t w, void *stream) {
+    static const char fn[] = "psa_attn_fused_backward";
+    fa2_status st = check_psa(fn, dt, batch, num_heads, key_dim, h, w);
+    if (st != FA2_OK) return st;
+    if (dt == FA2_F32) return fail(FA2_ERR_UNSUPPORTED, fn, "dtype must be F16 or BF16");
+    if (key_dim != 32) return fail(FA2_ERR_UNSUPPORTED, fn, "key_dim must be 32");
+    if ((int64_t)h * w > fa2mi::kPsaFusedBwdMaxPixels) return fail(FA2_ERR_UNSUPPORTED, fn, "h * w must be <= 512");
+    REQUIRE_PTR(fn, qkv);
+    REQUIRE_PTR(fn, out);
+    REQUIRE_PTR(fn, d_out);
+    REQUIRE_PTR(fn, d_qkv);
+    if (lse == nullptr || delta == nullptr) return fail(FA2_ERR_INVALID_ARG, fn, "lse and delta must not be NULL");
+    if (((reinterpret_cast<uintptr_t>(lse) | reinterpret_cast<uintptr_t>(delta)) & 3u) != 0)
+        return fail(FA2_ERR_INVALID_ARG, fn, "lse and delta must be 4-byte aligned");
+    const fa2mi::PsaShape s{batch, num_heads, key_dim, h * w};
+    return launched(fn, fa2mi::launch_psa_fused_backward((int)dt, qkv, out, lse, d_out, d_qkv, delta, s,
+                                                         (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -12,10 +12,10 @@ Legs measured in the same run (not part of `value`): the forward alone at
 that shape, cross-attention (BH 1024, Nq 1024, Nk 8192, D 64, K x 3), the
 backward-config step (BH 256, N 2048, D 128), the C2PSA block (pack,
 attention twice, merge, and the fused kernel) warm and with L2/MALL flushed
-before each call, a decoding shape (32 heads, 1 query row, 32768 keys,
-D 128) through the key-split forward and the plain forward, and a reference
-bf16 GEMM (random and constant operands) that shows the chip's practical
-dense-MFMA ceiling on random data.
+before each call, and its backward (composed and fused), a decoding shape
+(32 heads, 1 query row, 32768 keys, D 128) through the key-split forward and
+the plain forward, and a reference bf16 GEMM (random and constant operands)
+that shows the chip's practical dense-MFMA ceiling on random data.
 
 The CPU baseline times the fp64 oracle on a bounded sample of the same
 workload (a few heads at full sequence length) on the host cores.
@@ -420,6 +420,17 @@ def _leg_c2(torch, fa2, workloads, dev, legs):
     d_out = torch.randn((w2.batch, w2.out_channels, w2.h, w2.w), generator=g, device=dev).to(w2.torch_dtype)
     bwd_warm = _time_fn(torch, lambda: fa2.psa_block_backward(d_out, w2.num_heads, w2.key_dim, ws), 50)
     bwd_stream = _time_batch(torch, lambda: fa2.psa_block_backward(d_out, w2.num_heads, w2.key_dim, ws), 200)
+    # fused backward (three kernels, NCHW in and out) from the fused forward
+    lse_f = torch.empty((w2.bh, w2.n), dtype=torch.float32, device=dev)
+    fa2.psa_attn_fused(qkv, w2.num_heads, w2.key_dim, out_f, lse_f)
+    d_qkv = torch.empty_like(qkv)
+    delta = torch.empty((w2.bh, w2.n), dtype=torch.float32, device=dev)
+
+    def fbwd():
+        fa2.psa_attn_fused_backward(qkv, out_f, lse_f, d_out, w2.num_heads, w2.key_dim, d_qkv, delta)
+
+    fbwd_warm = _time_fn(torch, fbwd, 50)
+    fbwd_stream = _time_batch(torch, fbwd, 200)
     legs["c2"] = {
         "fused_us_per_call_stream": round(fused_stream * 1e3, 2),
         "block_us_per_call_stream": round(block_stream * 1e3, 2),
@@ -436,6 +447,8 @@ def _leg_c2(torch, fa2, workloads, dev, legs):
         "attn_tflops_warm": round(w2.attn_flops() / (warm * 1e-3) / 1e12, 2),
         "bwd_us_per_call_warm": round(bwd_warm * 1e3, 2),
         "bwd_us_per_call_stream": round(bwd_stream * 1e3, 2),
+        "fused_bwd_us_per_call_warm": round(fbwd_warm * 1e3, 2),
+        "fused_bwd_us_per_call_stream": round(fbwd_stream * 1e3, 2),
     }
     print(f"[bench] leg c2 {legs['c2']}", file=sys.stderr, flush=True)
 

@@ -211,6 +211,31 @@ fa2_status psa_attn_fused(fa2_dtype dt, const void *qkv, void *out, float *lse,
                           void *stream);
 
 /*
+ * Fused backward of the PSA attention block (vision_rs psa.rs, the block's
+ * backward hooks psa_merge_attn_backward -> psa_fa2_backward for V_lo and
+ * V_hi -> psa_pack_qkv_backward; vision-rs flash_attn2.rs "Backward - dQ",
+ * "Backward - dK / dV"). Given qkv, the block output `out` and its `lse`
+ * from psa_attn_fused, and d_out (the gradient of out, NCHW like out), writes
+ * d_qkv [batch, num_heads*4*key_dim, h, w], the gradient with respect to
+ * qkv: its Q, K, V_lo and V_hi channels, fully overwritten. With
+ * p_ij = exp(scale q_i.k_j - lse_i), scale = 1/sqrt(key_dim), and v, d_out
+ * the 2*key_dim value channels of a head:
+ *   delta_i = sum_c out_ic d_out_ic,   dS_ij = p_ij (d_out_i.v_j - delta_i),
+ *   dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i,
+ *   dv_j = sum_i p_ij d_out_i
+ * (the sum of the two value halves' gradients of the pages' V-split, since
+ * both halves share p). `delta` is a caller-owned float32 [batch*num_heads,
+ * h*w] buffer (4-byte aligned) that receives delta. Three kernels, no
+ * atomics, deterministic. dt F16 or BF16; key_dim 32; h*w <= 512, else
+ * FA2_ERR_UNSUPPORTED (psa_block_backward's composition covers the rest).
+ * A V-extraction gradient is added afterwards with psa_extract_v_backward.
+ */
+fa2_status psa_attn_fused_backward(fa2_dtype dt, const void *qkv, const void *out, const float *lse,
+                                   const void *d_out, void *d_qkv, float *delta,
+                                   int32_t batch, int32_t num_heads, int32_t key_dim, int32_t h, int32_t w,
+                                   void *stream);
+
+/*
  * Backward of psa_merge_attn (vision_rs psa.rs, "psa_merge_attn_backward"):
  * d_out is the gradient of the merged NCHW output, [batch,
  * num_heads*2*key_dim, h, w]; writes the gradients of the two attention

@@ -97,6 +97,16 @@ def test_bwd_and_psa_reject_invalid_arguments():
     assert lib.psa_extract_v_nchw(1, A, A, 16, 4, 16, 20, 20, None) == UNSUPPORTED
     assert lib.psa_extract_v_backward(2, MIS, A, 16, 4, 32, 20, 20, None) == INVALID
     assert lib.psa_extract_v_backward(2, A, A, 16, 4, 32, -1, 20, None) == INVALID
+    fb = lib.psa_attn_fused_backward
+    assert fb(0, A, A, A, A, A, A, 16, 4, 32, 20, 20, None) == UNSUPPORTED      # f32
+    assert fb(1, A, A, A, A, A, A, 16, 4, 64, 20, 20, None) == UNSUPPORTED      # key_dim 64
+    assert fb(1, A, A, A, A, A, A, 16, 4, 32, 16, 33, None) == UNSUPPORTED      # 528 pixels
+    assert fb(1, A, A, None, A, A, A, 16, 4, 32, 20, 20, None) == INVALID       # lse
+    assert fb(2, A, A, A, A, A, A + 2, 16, 4, 32, 20, 20, None) == INVALID      # delta misaligned
+    assert fb(2, A, MIS, A, A, A, A, 16, 4, 32, 20, 20, None) == INVALID        # out misaligned
+    assert fb(2, A, A, A, A, None, A, 16, 4, 32, 20, 20, None) == INVALID       # d_qkv
+    assert fb(2, A, A, A, A, A, A, 0, 4, 32, 20, 20, None) == INVALID
+    assert b"psa_attn_fused_backward" in lib.fa2_last_error()
 
 
 def _plan(dt, bh, n_q, n_k, d, splits):

@@ -293,6 +293,27 @@ def test_fwd_splitkv_decode_full():
     _err("O (fa2_fwd)", _np(o1), o_ref, 2e-2, case)
 
 
+def test_attention_fwd_takes_the_key_split_path_for_decoding():
+    """attention_fwd routes a decoding shape through the key-split forward
+    (same result as fa2_fwd_splitkv, bit for bit) and a large shape through
+    fa2_fwd."""
+    x = _inputs("bf16", 4, 2, 9000, 128, seed=43)
+    assert fa2.fa2_fwd_splitkv_plan(torch.bfloat16, 4, 2, 9000, 128, 0)[0] > 1
+    o, lse = fa2.attention_fwd(x["q"], x["k"], x["v"])
+    o2, lse2 = fa2.fa2_fwd_splitkv(x["q"], x["k"], x["v"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    o_ref, lse_ref = oracle.attention_fwd(x["q"], x["k"], x["v"], 1 / math.sqrt(128))
+    _err("O", _np(o), o_ref, 2e-2, "attention_fwd decode")
+    _err("LSE", _np(lse), lse_ref, 2e-2, "attention_fwd decode")
+    y = _inputs("bf16", 256, 256, 256, 64, seed=44)
+    assert fa2.fa2_fwd_splitkv_plan(torch.bfloat16, 256, 256, 256, 64, 0)[0] == 1
+    o, lse = fa2.attention_fwd(y["q"], y["k"], y["v"])
+    o2, lse2 = fa2.fa2_fwd(y["q"], y["k"], y["v"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
 def test_fwd_splitkv_workspace_reuse():
     """Two calls in a row on one workspace, the second smaller: the second
     result does not depend on what the first left behind."""
@@ -612,6 +633,71 @@ def test_psa_block_backward(dt, kd, b, nh, h, w):
     d_qkv2 = fa2.psa_block_backward(d_out, nh, kd, ws)
     torch.cuda.synchronize()
     assert torch.equal(first, d_qkv2)
+
+
+PSA_FUSED_BWD_SHAPES = [(16, 4, 20, 20), (2, 3, 5, 7), (1, 2, 8, 8), (1, 2, 5, 13), (2, 1, 16, 16),
+                        (1, 1, 1, 257), (1, 2, 16, 28), (1, 1, 16, 32)]
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("b,nh,h,w", PSA_FUSED_BWD_SHAPES, ids=lambda v: str(v))
+def test_psa_attn_fused_backward(dt, b, nh, h, w):
+    """The fused block backward (three kernels, NCHW in and out) against the
+    oracle's fp64 chain rule of the block; maps from 35 to 512 pixels cover
+    every whole-map capacity (64, 128, 256, 512) with and without 16-byte
+    aligned rows. Also: delta is rowsum(out * d_out), and a second call gives
+    the same bits."""
+    kd = 32
+    dtype = DTYPES[dt]
+    case = f"psa fused bwd {dt} b={b} nh={nh} h={h} w={w}"
+    print(case, flush=True)
+    wl = workloads.PsaWorkload("case", b, nh, kd, h, w, dt, seed=71 + h * w)
+    qkv = workloads.psa_inputs(wl, device=DEV)
+    g = torch.Generator(device="cpu").manual_seed(72 + h * w)
+    d_out = torch.randn(b, nh * 2 * kd, h, w, generator=g).to(DEV, dtype)
+    lse = torch.empty(b * nh, h * w, dtype=torch.float32, device=DEV)
+    out = fa2.psa_attn_fused(qkv, nh, kd, lse=lse)
+    delta = torch.full((b * nh, h * w), float("nan"), dtype=torch.float32, device=DEV)
+    d_qkv = torch.full_like(qkv, float("nan"))
+    fa2.psa_attn_fused_backward(qkv, out, lse, d_out, nh, kd, d_qkv=d_qkv, delta=delta)
+    torch.cuda.synchronize()
+    want = oracle.psa_block_backward(qkv, nh, kd, d_out)
+    _err("d_qkv", _np(d_qkv), want, TOL[dtype], case)
+    rows = (out.double() * d_out.double()).view(b, nh, 2 * kd, h * w).sum(2).reshape(b * nh, h * w)
+    assert torch.allclose(delta.double(), rows, atol=1e-3, rtol=1e-4), case
+    again = fa2.psa_attn_fused_backward(qkv, out, lse, d_out, nh, kd)
+    torch.cuda.synchronize()
+    assert torch.equal(again, d_qkv), case
+
+
+def test_psa_attn_fused_backward_matches_composed_path():
+    """At C2, the fused backward and psa_block_backward (eight launches on the
+    pages' V-split) agree within the bar."""
+    w2 = workloads.C2
+    qkv = workloads.psa_inputs(w2, device=DEV)
+    g = torch.Generator(device="cpu").manual_seed(81)
+    d_out = torch.randn(w2.batch, w2.out_channels, w2.h, w2.w, generator=g).to(DEV, w2.torch_dtype)
+    lse = torch.empty(w2.bh, w2.n, dtype=torch.float32, device=DEV)
+    out = fa2.psa_attn_fused(qkv, w2.num_heads, w2.key_dim, lse=lse)
+    fused = fa2.psa_attn_fused_backward(qkv, out, lse, d_out, w2.num_heads, w2.key_dim)
+    ws = {}
+    fa2.psa_block(qkv, w2.num_heads, w2.key_dim, ws)
+    composed = fa2.psa_block_backward(d_out, w2.num_heads, w2.key_dim, ws)
+    torch.cuda.synchronize()
+    _err("d_qkv fused vs composed", _np(fused), _np(composed), 2e-2, "C2")
+
+
+def test_psa_attn_fused_backward_rejects_unsupported():
+    qkv = torch.zeros(1, 4 * 64, 4, 4, dtype=torch.float16, device=DEV)
+    out = torch.zeros(1, 2 * 64, 4, 4, dtype=torch.float16, device=DEV)
+    lse = torch.zeros(1, 16, dtype=torch.float32, device=DEV)
+    with pytest.raises(fa2.Fa2Error, match="key_dim must be 32"):
+        fa2.psa_attn_fused_backward(qkv, out, lse, out, 1, 64)
+    qkv = torch.zeros(1, 4 * 32, 1, 513, dtype=torch.float16, device=DEV)
+    out = torch.zeros(1, 2 * 32, 1, 513, dtype=torch.float16, device=DEV)
+    lse = torch.zeros(1, 513, dtype=torch.float32, device=DEV)
+    with pytest.raises(fa2.Fa2Error, match="512"):
+        fa2.psa_attn_fused_backward(qkv, out, lse, out, 1, 32)
 
 
 def test_psa_block_backward_needs_forward_workspace():
