@@ -82,22 +82,38 @@ __global__ __launch_bounds__(256) void delta_kernel(const typename Traits<DT>::e
 // ds_read_b64_tr_b16. The gfx950 LDS behaves as 64 four-byte banks;
 // ds_read_b128 serves 16 lanes per cycle (16 consecutive rows, one 16-byte
 // chunk each) and ds_read_b64_tr_b16 32 lanes per cycle (4 consecutive rows,
-// 64 bytes each). A row stride of an odd number of 16-byte chunks keeps the
-// first pattern conflict-free; with 19 chunks at D = 128 (9 at 64, 5 at 32)
-// the second is at most 2-way. (An XOR swizzle removes both conflicts but
-// costs more address arithmetic than the conflicts it saves.) float32:
-// padded row-major tiles plus a transposed copy (stride LDT).
-template <Dt DT, int D>
+// 64 bytes each). Two layouts:
+//  SHIFT: the row stride is an odd multiple of 64 bytes (the transposing
+//    reads' 4 rows fill 256 bytes) and rows are shifted by row_shift (the 16
+//    rows of a row read fill 16 distinct 16-byte slots): no bank conflict
+//    for either pattern (dkdv, 1.8% faster at N 4096, D 128);
+//  plain: a row stride of an odd number of 16-byte chunks (19 at D = 128,
+//    9 at 64, 5 at 32): row reads conflict-free, transposing reads at most
+//    2-way, less address arithmetic (dq, 0.8% faster than shifted).
+// float32: padded row-major tiles plus a transposed copy (stride LDT).
+template <Dt DT, int D, bool SHIFT>
 struct BwdTile {
     using elem = typename Traits<DT>::elem;
     using frag = typename Traits<DT>::frag;
     static constexpr bool TR = sizeof(elem) == 2;
+    static constexpr bool SH = TR && SHIFT;
     static constexpr int VEC = vec_elems<DT>();
-    static constexpr int LD = TR ? (D == 128 ? D + 3 * VEC : D + VEC) : D + VEC;  // row stride
+    // shifted: the smallest odd multiple of 64 bytes that holds a row plus
+    // the largest shift (48 bytes)
+    static constexpr int LD_UNITS = (2 * D + 48 + 63) / 64;
+    static constexpr int LD =
+        SH ? 32 * (LD_UNITS | 1) : (TR ? (D == 128 ? D + 3 * VEC : D + VEC) : D + VEC);  // row stride
+
+    __device__ static __forceinline__ const elem *row_ptr(const elem *tile, int row) {
+        if constexpr (SH)
+            return tile + row * LD + row_shift(row);
+        else
+            return tile + row * LD;
+    }
 
     // row fragment (contraction step t over head_dim) of tile row `row`
     __device__ static __forceinline__ frag row(const elem *tile, int row, int t, int h) {
-        return ld_row_frag<DT>(tile + row * LD, t, h);
+        return ld_row_frag<DT>(row_ptr(tile, row), t, h);
     }
 
     // A fragment of T^T: columns 32db.. of the tile x its rows 32kb + 16t ..
@@ -105,7 +121,10 @@ struct BwdTile {
     template <int LDT>
     __device__ static __forceinline__ frag trans(const elem *tile, const elem *ttile, int kb, int t, int db,
                                                  int lane) {
-        if constexpr (TR) {
+        if constexpr (SH) {
+            (void)ttile;
+            return ld_vt_frag_tr_sh<DT>(tile, LD, 32 * kb + 16 * t, 32 * db, lane);
+        } else if constexpr (TR) {
             (void)ttile;
             return ld_vt_frag_tr<DT>(tile, LD, 32 * kb + 16 * t, 32 * db, lane);
         } else {
@@ -116,7 +135,18 @@ struct BwdTile {
 
     template <int R, int NT>
     __device__ static __forceinline__ void store(const RowStage<DT, R, D, NT> &st, elem *tile, int tid) {
-        st.template store<LD>(tile, tid);
+        using St = RowStage<DT, R, D, NT>;
+        if constexpr (SH) {
+#pragma unroll
+            for (int i = 0; i < St::PER_THREAD; ++i) {
+                const int pc = tid + i * NT;
+                const int row = pc / (D / VEC), cv = pc % (D / VEC);
+                if (St::PIECES % NT == 0 || pc < St::PIECES)
+                    *reinterpret_cast<uint4 *>(tile + row * LD + row_shift(row) + cv * VEC) = st.v[i];
+            }
+        } else {
+            st.template store<LD>(tile, tid);
+        }
     }
 };
 
@@ -140,7 +170,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     constexpr int BR = 32 * WAVES;
     constexpr int KPL = Tr::KPL;
     constexpr int KSTEP = 2 * KPL;
-    using Tl = BwdTile<DT, D>;
+    using Tl = BwdTile<DT, D, false>;
     constexpr int LDT = BC + 4;          // float32 transposed K copy
     constexpr int KS = BC * Tl::LD;
     constexpr int TSZ = TR ? 1 : D * LDT;
@@ -273,7 +303,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     constexpr int BKV = 32 * WAVES;
     constexpr int KPL = Tr::KPL;
     constexpr int KSTEP = 2 * KPL;
-    using Tl = BwdTile<DT, D>;
+    using Tl = BwdTile<DT, D, true>;
     constexpr int LDT = BQ + 4;          // float32 transposed copies
     constexpr int QS = BQ * Tl::LD;
     constexpr int TSZ = TR ? 1 : D * LDT;
@@ -328,7 +358,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
         Tl::store(vst, Vk, tid);
         // made visible by the barrier after the first query tile is staged
     }
-    const elem *vkrow = Vk + (wave * 32 + col) * Tl::LD;
+    const elem *vkrow = Tl::row_ptr(Vk, wave * 32 + col);
 
     f32x16 accK[NDB], accV[NDB];
 #pragma unroll

@@ -150,6 +150,35 @@ __device__ __forceinline__ typename Traits<DT>::frag c_to_frag(const f32x16 &c, 
     }
 }
 
+// Shifted LDS rows: row r of a tile with row stride LD (an odd multiple of
+// 64 bytes) starts at r * LD + row_shift(r) elements (16-bit types), a
+// 16-byte shift that cycles every 4 rows. ds_read_b64_tr_b16 takes 4
+// consecutive rows at a time: one shift, rows 64 bytes apart modulo 256, no
+// bank conflict. Row reads of 16 (ds_read_b128) or 32 (8-byte reads)
+// consecutive rows at one column land 64 (r mod 4) + 16 ((r / 4) mod 4) bytes
+// apart modulo 256: 16 distinct 16-byte slots instead of 4. The shift only
+// depends on bits 2-3 of the row, so for rows 16k + lane terms it is a
+// per-lane constant. LD must leave 24 elements of room past the data.
+__device__ __forceinline__ constexpr int row_shift(int r) { return 8 * ((r >> 2) & 3); }
+
+// ld_vt_frag_tr on a tile with shifted rows.
+template <Dt DT>
+__device__ __forceinline__ typename Traits<DT>::frag ld_vt_frag_tr_sh(const typename Traits<DT>::elem *vtile, int LD,
+                                                                       int key0, int d0, int lane) {
+    static_assert(Traits<DT>::KPL == 8, "16-bit element types only");
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    using lds_i16x4 = __attribute__((address_space(3))) i16x4;
+    const int l = lane & 15, g = lane >> 4, hh = g >> 1;
+    const int r = key0 + 4 * hh + (l >> 2);
+    const int c = d0 + 16 * (g & 1) + 4 * (l & 3);
+    const typename Traits<DT>::elem *p0 = vtile + r * LD + row_shift(r) + c;
+    const typename Traits<DT>::elem *p1 = vtile + (r + 8) * LD + row_shift(r + 8) + c;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p0));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p1));
+    return __builtin_bit_cast(typename Traits<DT>::frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // ---------------------------------------------------------------------------
 // Cooperative tile staging: an R x D row-major global tile is moved by the
 // workgroup in RB-row x VEC-column blocks (VEC = one 16-byte vector), each

@@ -51,32 +51,10 @@ __global__ __launch_bounds__(256) void psa_delta_kernel(const T *__restrict__ ou
     delta[(int64_t)bh * hw + p] = acc;
 }
 
-// LDS layout of the channel-major operands: row r of an array with row stride
-// LD (an odd multiple of 64 bytes) starts at r * LD + row_shift(r) elements,
-// a 16-byte shift that cycles every 4 rows. The transposing reads take 4
-// consecutive rows at a time (one shift, rows still 64 bytes apart modulo
-// 256: conflict-free); the row reads take 32 consecutive rows at once, which
-// without the shift fall into 4 bank groups (8-way conflicts) and with it
-// into 16 (2-way). LD leaves room for the largest shift (24 elements).
-__device__ __forceinline__ constexpr int row_shift(int r) { return 8 * ((r >> 2) & 3); }
-
-// ds_read_b64_tr_b16 fragment (as ld_vt_frag_tr) from a shifted array: rows
-// (channels) ch0 + .., columns (pixels) px0 + ..
-template <Dt DT>
-__device__ __forceinline__ typename Traits<DT>::frag ld_tr_sh(const typename Traits<DT>::elem *tile, int LD, int ch0,
-                                                               int px0, int lane) {
-    typedef short i16x4 __attribute__((ext_vector_type(4)));
-    typedef short i16x8 __attribute__((ext_vector_type(8)));
-    using lds_i16x4 = __attribute__((address_space(3))) i16x4;
-    const int l = lane & 15, g = lane >> 4, hh = g >> 1;
-    const int r = ch0 + 4 * hh + (l >> 2);
-    const int c = px0 + 16 * (g & 1) + 4 * (l & 3);
-    const typename Traits<DT>::elem *p0 = tile + r * LD + row_shift(r) + c;
-    const typename Traits<DT>::elem *p1 = tile + (r + 8) * LD + row_shift(r + 8) + c;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p0));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p1));
-    return __builtin_bit_cast(typename Traits<DT>::frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
+// The channel-major operand arrays use shifted rows (row_shift): the
+// transposing reads take 4 consecutive rows at a time, the row reads 32
+// consecutive rows at once, and both stay free of bank conflicts (without
+// the shift the row reads on these 64-byte-odd strides are 8-way).
 
 // Row fragment (as ld_t_frag) of row `row` of a shifted array.
 template <Dt DT>
@@ -216,18 +194,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (active) {
         frag qf[KD / 16], df[DV / 16];
 #pragma unroll
-        for (int t = 0; t < KD / 16; ++t) qf[t] = ld_tr_sh<DT>(Qt, LDB, 16 * t, 32 * qs, lane);
+        for (int t = 0; t < KD / 16; ++t) qf[t] = ld_vt_frag_tr_sh<DT>(Qt, LDB, 16 * t, 32 * qs, lane);
 #pragma unroll
-        for (int t = 0; t < DV / 16; ++t) df[t] = ld_tr_sh<DT>(Dt_, LDB, 16 * t, 32 * qs, lane);
+        for (int t = 0; t < DV / 16; ++t) df[t] = ld_vt_frag_tr_sh<DT>(Dt_, LDB, 16 * t, 32 * qs, lane);
 #pragma unroll
         for (int kb = 0; kb < C::NBH; ++kb) {
             if (kb >= nb) break;
             const int key0 = 32 * (kb0 + kb);
             f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-            for (int t = 0; t < KD / 16; ++t) s = Tr::mfma(ld_tr_sh<DT>(Kt, LDW, 16 * t, key0, lane), qf[t], s);
+            for (int t = 0; t < KD / 16; ++t) s = Tr::mfma(ld_vt_frag_tr_sh<DT>(Kt, LDW, 16 * t, key0, lane), qf[t], s);
 #pragma unroll
-            for (int t = 0; t < DV / 16; ++t) dp = Tr::mfma(ld_tr_sh<DT>(Vt, LDW, 16 * t, key0, lane), df[t], dp);
+            for (int t = 0; t < DV / 16; ++t) dp = Tr::mfma(ld_vt_frag_tr_sh<DT>(Vt, LDW, 16 * t, key0, lane), df[t], dp);
 #pragma unroll
             for (int c = 0; c < 16; ++c) {
                 const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c], scale_log2, -lse2));
@@ -336,9 +314,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (active) {
         frag kf[KD / 16], vf[DV / 16];
 #pragma unroll
-        for (int t = 0; t < KD / 16; ++t) kf[t] = ld_tr_sh<DT>(Kt, LDB, 16 * t, 32 * ks, lane);
+        for (int t = 0; t < KD / 16; ++t) kf[t] = ld_vt_frag_tr_sh<DT>(Kt, LDB, 16 * t, 32 * ks, lane);
 #pragma unroll
-        for (int t = 0; t < DV / 16; ++t) vf[t] = ld_tr_sh<DT>(Vt, LDB, 16 * t, 32 * ks, lane);
+        for (int t = 0; t < DV / 16; ++t) vf[t] = ld_vt_frag_tr_sh<DT>(Vt, LDB, 16 * t, 32 * ks, lane);
 #pragma unroll
         for (int qb = 0; qb < C::NBH; ++qb) {
             if (qb >= nb) break;
@@ -346,9 +324,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             f32x16 s = zero16(), dp = zero16();
 #pragma unroll
             for (int t = 0; t < KD / 16; ++t)
-                s = Tr::mfma(ld_tr_sh<DT>(Qt, LDW, 16 * t, 32 * qblock, lane), kf[t], s);
+                s = Tr::mfma(ld_vt_frag_tr_sh<DT>(Qt, LDW, 16 * t, 32 * qblock, lane), kf[t], s);
 #pragma unroll
-            for (int t = 0; t < DV / 16; ++t) dp = Tr::mfma(ld_tr_sh<DT>(Dt_, LDW, 16 * t, 32 * qblock, lane), vf[t], dp);
+            for (int t = 0; t < DV / 16; ++t) dp = Tr::mfma(ld_vt_frag_tr_sh<DT>(Dt_, LDW, 16 * t, 32 * qblock, lane), vf[t], dp);
             // register c of lane half h is query 32 qblock + crow(c, h)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
