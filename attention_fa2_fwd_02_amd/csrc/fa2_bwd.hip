@@ -223,7 +223,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     auto load = [&](int row0) {
         kst.load(krs, row0, tid);
         vst.load(vrs, row0, tid);
-        if constexpr (!TR) ktst.load(K + koff + (int64_t)row0 * D, n_k - row0, tid);
+        if constexpr (!TR) ktst.load(krs, row0, tid);
     };
     auto store = [&](int stage) {
         Tl::store(kst, Ks + stage * KS, tid);
@@ -383,8 +383,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
             dreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ers, (row0 + tid) * 4, 0, 0));
         }
         if constexpr (!TR) {
-            qtst.load(Q + qoff + (int64_t)row0 * D, n_q - row0, tid);
-            dtst.load(dO + qoff + (int64_t)row0 * D, n_q - row0, tid);
+            qtst.load(qrs, row0, tid);
+            dtst.load(drs, row0, tid);
         }
     };
     auto store = [&](int stage) {

@@ -182,7 +182,8 @@ __device__ __forceinline__ typename Traits<DT>::frag ld_vt_frag_tr_sh(const type
 // ---------------------------------------------------------------------------
 // Cooperative tile staging: an R x D row-major global tile is moved by the
 // workgroup in RB-row x VEC-column blocks (VEC = one 16-byte vector), each
-// thread owning whole blocks. Rows at or beyond `valid` are zero-filled.
+// thread owning whole blocks. Loads are buffer loads: rows past the end of
+// the buffer read as zero, with no lane-dependent branch.
 // COL_FAST numbers blocks along a row first (neighbouring lanes read
 // neighbouring 16-byte pieces of one row: best for tiles kept row-major in
 // LDS); otherwise down a column first (neighbouring lanes write neighbouring
@@ -201,22 +202,10 @@ struct TileStage {
     __device__ static constexpr int row_block(int blk) { return COL_FAST ? blk / (D / VEC) : blk % (R / RB); }
     __device__ static constexpr int col_block(int blk) { return COL_FAST ? blk % (D / VEC) : blk / (R / RB); }
 
-    // Global -> registers. `base` points at row 0 of the tile; row stride D.
-    __device__ __forceinline__ void load(const elem *__restrict__ base, int valid, int tid) {
-#pragma unroll
-        for (int i = 0; i < PER_THREAD; ++i) {
-            const int blk = tid + i * NT;
-            const int rb = row_block(blk), cb = col_block(blk);
-#pragma unroll
-            for (int r = 0; r < RB; ++r) {
-                const int row = rb * RB + r;
-                if ((BLOCKS % NT == 0 || blk < BLOCKS) && row < valid)
-                    v[i][r] = *reinterpret_cast<const uint4 *>(base + (int64_t)row * D + cb * VEC);
-                else
-                    v[i][r] = make_uint4(0, 0, 0, 0);
-            }
-        }
-    }
+    // Global -> registers: rows row0 .. row0 + R - 1 of the buffer `rsrc`
+    // covers (row stride D; rows past its end read as zero, so there is no
+    // lane-dependent branch). Byte offsets are 32-bit, as for RowStage.
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, int row0, int tid);
 
     // Registers -> LDS, row-major with row stride LD (elements).
     template <int LD>
@@ -294,6 +283,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 
 __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+template <Dt DT, int R, int D, int NT, bool COL_FAST, int RB>
+__device__ __forceinline__ void TileStage<DT, R, D, NT, COL_FAST, RB>::load(__amdgpu_buffer_rsrc_t rsrc, int row0,
+                                                                             int tid) {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) {
+        const int blk = tid + i * NT;
+        const int rb = row_block(blk), cb = col_block(blk);
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const int row = rb * RB + r;
+            if (BLOCKS % NT == 0 || blk < BLOCKS)
+                v[i][r] = buffer_load16(rsrc, ((uint32_t)(row0 + row) * D + cb * VEC) * (uint32_t)sizeof(elem));
+            else
+                v[i][r] = make_uint4(0, 0, 0, 0);
+        }
+    }
 }
 
 // Row-major R x D tile staging through registers with buffer loads: thread

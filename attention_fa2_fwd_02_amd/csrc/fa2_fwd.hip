@@ -11,9 +11,12 @@
 //      (the C column), so a row's max needs one exchange between lane halves.
 //   3. Online softmax in the log2 domain (scale*log2(e) folded into one FMA
 //      before exp2): P = 2^(S - m), l += rowsum(P) over P as rounded to the
-//      element type for the product (lane-partial sums, combined at the end). The reference max m is raised lazily: only when
-//      a row max exceeds it by more than kRescaleLog2, and then O and l are
-//      rescaled by 2^(m - m') as in the online-softmax recurrence.
+//      element type for the product (lane-partial sums, combined at the
+//      end). The reference m is the first tile's row max; later tiles use
+//      it as it is unless l leaves range, in which case the workgroup redoes
+//      the rows with the max taken on every tile and m raised lazily (only
+//      when a row max exceeds it by more than kRescaleLog2, O and l then
+//      rescaled by 2^(m - m') as in the online-softmax recurrence).
 //   4. O^T += V^T P^T on MFMA, P fed from registers as the B operand.
 // Epilogue: O = O^T / l rounded to the element type; LSE = ln2 * (m + log2 l).
 #include <type_traits>
@@ -64,12 +67,14 @@ constexpr int fwd_ldv() {
 
 // One key tile of the forward for one wave: scores, online softmax with lazy
 // rescaling, and the P V accumulation. MASK: the tile is the ragged last one
-// and keys at or beyond kvalid do not exist (probability 0).
-template <Dt DT, int D, int BC, bool MASK>
+// and keys at or beyond kvalid do not exist (probability 0). FAST: the row
+// max is taken only when `first` (wave-uniform) is set; otherwise the
+// probabilities use the current reference as they are (see fwd_kernel).
+template <Dt DT, int D, int BC, bool MASK, bool FAST = false>
 __device__ __forceinline__ void fwd_tile(const typename Traits<DT>::elem *kt, const typename Traits<DT>::elem *vt,
                                          const typename Traits<DT>::frag (&qf)[D / (2 * Traits<DT>::KPL)],
                                          f32x16 (&acc)[D / 32], float &m_ref, float &l_run, float scale_log2,
-                                         int kvalid, int lane) {
+                                         int kvalid, int lane, bool first = true) {
     using Tr = Traits<DT>;
     using elem = typename Tr::elem;
     using frag = typename Tr::frag;
@@ -103,28 +108,30 @@ __device__ __forceinline__ void fwd_tile(const typename Traits<DT>::elem *kt, co
             for (int c = 0; c < 16; ++c)
                 if (32 * kb + crow(c, h) >= kvalid) s[kb][c] = -INFINITY;
     }
-    // lane-partial max of the raw scores (scale > 0, so the max commutes
-    // with scaling)
-    float mx = -INFINITY;
+    if (!FAST || first) {
+        // lane-partial max of the raw scores (scale > 0, so the max commutes
+        // with scaling)
+        float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int c = 0; c < 16; ++c) mx = fmaxf(mx, s[kb][c]);
-    // Lazy rescaling: the reference max only moves when some row's max
-    // exceeds it by more than kRescaleLog2 (probabilities then stay
-    // <= 2^kRescaleLog2). Moving it rescales O and l by 2^(m_ref - m_new),
-    // the online-softmax correction; the final O = acc / l is unchanged.
-    const float mx2 = mx * scale_log2;
-    if (__any(mx2 > m_ref + kRescaleLog2)) {
-        __asm__ volatile("" ::: "memory");
-        const float m_new = fmaxf(m_ref, xhalf_max(mx2));
-        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+            for (int c = 0; c < 16; ++c) mx = fmaxf(mx, s[kb][c]);
+        // Lazy rescaling: the reference max only moves when some row's max
+        // exceeds it by more than kRescaleLog2 (probabilities then stay
+        // <= 2^kRescaleLog2). Moving it rescales O and l by 2^(m_ref - m_new),
+        // the online-softmax correction; the final O = acc / l is unchanged.
+        const float mx2 = mx * scale_log2;
+        if (__any(mx2 > m_ref + kRescaleLog2)) {
+            __asm__ volatile("" ::: "memory");
+            const float m_new = fmaxf(m_ref, xhalf_max(mx2));
+            const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int c = 0; c < 16; ++c) acc[db][c] *= alpha;
-        l_run *= alpha;
-        m_ref = m_new;
+                for (int c = 0; c < 16; ++c) acc[db][c] *= alpha;
+            l_run *= alpha;
+            m_ref = m_new;
+        }
     }
     const float neg_m = -m_ref;
 #pragma unroll
@@ -217,11 +224,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     }
 
     f32x16 acc[NDB];
-#pragma unroll
-    for (int i = 0; i < NDB; ++i) acc[i] = zero16();
     // m_ref: the reference max (log2 units) the probabilities of this row are
     // taken against; l_run: lane-partial sum of those probabilities.
-    float m_ref = -INFINITY, l_run = 0.f;
+    float m_ref, l_run;
 
     // K/V tiles: buffer loads over this head's rows (rows past n_k read as
     // zero) into registers, then into one of two LDS stages.
@@ -232,12 +237,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     constexpr int RBS = stage_rows<DT, BC, D, NT>();
     using VStage = std::conditional_t<TR, RowStage<DT, BC, D, NT>, TileStage<DT, BC, D, NT, false, RBS>>;
     VStage vst;
-    auto vload = [&](int row0) {
-        if constexpr (TR)
-            vst.load(vrs, row0, tid);
-        else
-            vst.load(V + koff + (int64_t)row0 * D, klen - row0, tid);
-    };
+    auto vload = [&](int row0) { vst.load(vrs, row0, tid); };
     auto vstore = [&](elem *dst) {
         if constexpr (TR)
             vst.template store<LDV>(dst, tid);
@@ -247,36 +247,65 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 
     const int ntiles = (klen + BC - 1) / BC;
     const int nfull = klen / BC;  // full tiles; a ragged last one follows when klen % BC != 0
-    kst.load(krs, 0, tid);
-    vload(0);
-    kst.template store<LDK>(Ks, tid);
-    vstore(Vs);
-    if (ntiles > 1) {
-        kst.load(krs, BC, tid);
-        vload(BC);
-    }
-    __syncthreads();
-
-    for (int it = 0; it < nfull; ++it) {
-        const int j0 = it * BC;
-        fwd_tile<DT, D, BC, false>(Ks + (it & 1) * KS, Vs + (it & 1) * VS, qf, acc, m_ref, l_run, scale_log2, BC,
-                                   lane);
-        // next tile (already in registers) into the other stage; then fetch
-        // the one after. One barrier per tile: it orders this tile's reads of
-        // a stage before that stage is refilled two tiles later.
+    // Pass 0 takes the row max on the first tile (and on a ragged last one)
+    // only: later probabilities are 2^(s - m_ref) against that reference as
+    // they are. The reference only scales every probability of a row by the
+    // same power of two, which O = acc / l cancels, so this is the same
+    // softmax as long as the values stay in range. If some row of the
+    // workgroup ends with l above 2^100 or not finite (a score about 100 or
+    // more above the first tile's max, in log2 units), the workgroup runs
+    // pass 1: the recurrence with the max taken on every tile (lazy
+    // rescaling).
+    // next tile (already in registers) into the other stage, then fetch the
+    // one after. One barrier per tile: it orders this tile's reads of a stage
+    // before that stage is refilled two tiles later.
+    auto advance = [&](int it) {
         if (it + 1 < ntiles) {
             kst.template store<LDK>(Ks + ((it + 1) & 1) * KS, tid);
             vstore(Vs + ((it + 1) & 1) * VS);
             if (it + 2 < ntiles) {
-                kst.load(krs, j0 + 2 * BC, tid);
-                vload(j0 + 2 * BC);
+                kst.load(krs, (it + 2) * BC, tid);
+                vload((it + 2) * BC);
             }
         }
         __syncthreads();
+    };
+    auto run_pass = [&](auto fast_tag) {
+        constexpr bool FASTP = decltype(fast_tag)::value;
+#pragma unroll
+        for (int i = 0; i < NDB; ++i) acc[i] = zero16();
+        m_ref = -INFINITY;
+        l_run = 0.f;
+        kst.load(krs, 0, tid);
+        vload(0);
+        kst.template store<LDK>(Ks, tid);
+        vstore(Vs);
+        if (ntiles > 1) {
+            kst.load(krs, BC, tid);
+            vload(BC);
+        }
+        __syncthreads();
+        for (int it = 0; it < nfull; ++it) {
+            fwd_tile<DT, D, BC, false, FASTP>(Ks + (it & 1) * KS, Vs + (it & 1) * VS, qf, acc, m_ref, l_run,
+                                              scale_log2, BC, lane, it == 0);
+            advance(it);
+        }
+        if (nfull < ntiles)
+            fwd_tile<DT, D, BC, true>(Ks + (nfull & 1) * KS, Vs + (nfull & 1) * VS, qf, acc, m_ref, l_run,
+                                      scale_log2, klen - nfull * BC, lane);
+    };
+    if constexpr (TR) {
+        run_pass(std::true_type{});
+        // a barrier for the whole workgroup either way: pass 1 refills the
+        // stages
+        const bool bad = !(l_run <= 0x1p100f);  // also true for inf and NaN
+        if (__syncthreads_or(bad)) run_pass(std::false_type{});
+    } else {
+        // float32 keeps the single exact pass: the two-pass form gave wrong
+        // output channels at head_dim 64 with 4 or 8 waves (a code
+        // generation issue not pinned down; the exact pass is verified)
+        run_pass(std::false_type{});
     }
-    if (nfull < ntiles)
-        fwd_tile<DT, D, BC, true>(Ks + (nfull & 1) * KS, Vs + (nfull & 1) * VS, qf, acc, m_ref, l_run, scale_log2,
-                                  klen - nfull * BC, lane);
 
     const float l_tot = xhalf_sum(l_run);
     if (qrow < n_q) {

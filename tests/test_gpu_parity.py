@@ -470,6 +470,30 @@ def test_fwd_bwd_peaked_softmax(dt, d):
         _err(name, _np(got), want, tol, case)
 
 
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("mult", [6.0, 16.0])
+def test_fwd_scores_far_above_first_tile(dt, mult):
+    """Keys from 128 on are mult x query 0, so query 0's scores there exceed
+    the first key tile's max by about 70 (mult 6) or 190 (mult 16) in log2
+    units. The forward takes the first tile's max as the reference and only
+    reruns a workgroup with the per-tile max when l leaves range (always at
+    mult 16; at mult 6 only where the element type cannot hold the
+    probabilities, f16). Either way the result is the softmax."""
+    bh, nq, nk, d = 2, 70, 300, 64
+    case = f"far scores {dt} x{mult}"
+    print(case, flush=True)
+    x = _inputs(dt, bh, nq, nk, d, seed=91)
+    k = x["k"].clone()
+    k[:, 128:, :] = (mult * x["q"][:, :1, :].float()).to(k.dtype)
+    o, lse = fa2.fa2_fwd(x["q"], k, x["v"])
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_fwd(x["q"], k, x["v"], 1 / 8.0)
+    tol = TOL[DTYPES[dt]]
+    _err("O", _np(o), o_ref, tol, case)
+    # lse reaches a few hundred here: compare it relative to its size
+    _err("LSE", _np(lse), lse_ref, tol * max(1.0, float(np.abs(lse_ref).max()) / 8.0), case)
+
+
 def test_fwd_degenerate_inputs_full_length():
     """At the LLM sequence length with the 8-wave launch: Q = 0 and identical
     keys both make every row uniform, so O is the mean of V over the keys and
