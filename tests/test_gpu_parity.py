@@ -70,6 +70,25 @@ def test_fwd_small(dt, d, shape):
     _err("LSE", _np(lse), lse_ref, tol, case)
 
 
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("shape", [(256, 100, 150), (512, 90, 130)], ids=["4waves", "8waves"])
+def test_fwd_workgroup_sizes(dt, d, shape):
+    """Shapes whose head count selects 4-wave (128-row) and 8-wave (256-row)
+    workgroups in the plain forward, every output against the oracle (the
+    small shapes above run 2-wave workgroups)."""
+    bh, nq, nk = shape
+    case = f"fwd {dt} d={d} bh={bh} nq={nq} nk={nk}"
+    print(case, flush=True)
+    x = _inputs(dt, bh, nq, nk, d, seed=500 + bh + d)
+    o, lse = fa2.fa2_fwd(x["q"], x["k"], x["v"])
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_fwd(x["q"], x["k"], x["v"], 1 / math.sqrt(d))
+    tol = TOL[DTYPES[dt]]
+    _err("O", _np(o), o_ref, tol, case)
+    _err("LSE", _np(lse), lse_ref, tol, case)
+
+
 def test_fwd_c1_tiny_f32():
     w = workloads.C1
     x = workloads.attn_inputs(w, device=DEV)
