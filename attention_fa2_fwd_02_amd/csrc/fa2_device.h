@@ -167,7 +167,6 @@ __device__ __forceinline__ typename Traits<DT>::frag ld_vt_frag_tr_sh(const type
                                                                        int key0, int d0, int lane) {
     static_assert(Traits<DT>::KPL == 8, "16-bit element types only");
     typedef short i16x4 __attribute__((ext_vector_type(4)));
-    typedef short i16x8 __attribute__((ext_vector_type(8)));
     using lds_i16x4 = __attribute__((address_space(3))) i16x4;
     const int l = lane & 15, g = lane >> 4, hh = g >> 1;
     const int r = key0 + 4 * hh + (l >> 2);

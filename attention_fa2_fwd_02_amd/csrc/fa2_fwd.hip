@@ -256,8 +256,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     // more above the first tile's max, in log2 units), the workgroup runs
     // pass 1: the recurrence with the max taken on every tile (lazy
     // rescaling).
-    // next tile (already in registers) into the other stage, then fetch the
-    // one after. One barrier per tile: it orders this tile's reads of a stage
+    //
+    // After each tile: store the next tile (already in registers) into the
+    // other stage, then fetch the one after. One barrier per tile: it orders this tile's reads of a stage
     // before that stage is refilled two tiles later.
     auto advance = [&](int it) {
         if (it + 1 < ntiles) {

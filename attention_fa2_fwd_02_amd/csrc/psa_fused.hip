@@ -243,25 +243,45 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 }
 
 
+// Calls f(std::integral_constant<int, v>) for a wave-uniform 0 <= v < N, so
+// that register arrays can be indexed with v at compile time.
+template <int N, typename F>
+__device__ __forceinline__ void uniform_switch(int v, F &&f) {
+    if constexpr (N > 1) {
+        if (v == N - 1) {
+            f(std::integral_constant<int, N - 1>{});
+            return;
+        }
+        uniform_switch<N - 1>(v, f);
+    } else {
+        f(std::integral_constant<int, 0>{});
+    }
+}
+
 // Small feature maps (the usual C2PSA case: h*w of a few hundred pixels).
-// One workgroup per (head, 128 queries), 8 waves = 4 query sub-blocks of 32
-// x 2 key halves of at most NB blocks of 32 keys each (the map's
-// ceil(h*w / 32) blocks split evenly; a ragged last block is masked). The
-// head's whole K^T and V^T (zero past h*w) and the Q^T block are fetched into
-// LDS in one burst; each wave keeps the scores of its key half in registers,
-// so its softmax needs one exact row max and one exp2 pass, no online
-// rescaling; its block loops have wave-uniform trip counts. The two
-// key halves of a query sub-block are merged through LDS with the
-// online-softmax combination (max, rescaled sums), each wave finishing half
-// of the value channels and storing them straight to the pixel rows.
-template <int KD, int NB>
+// One workgroup per (head, 128 queries) with 4 KS waves = 4 query sub-blocks
+// of 32 x KS key slices (the map's ceil(h*w / 32) blocks of 32 keys split
+// evenly; a ragged last block is masked). Wave w runs on SIMD w % 4, so the
+// KS slices of one query sub-block share a SIMD. The head's whole K^T and
+// V^T (zero past h*w) and the Q^T block are fetched into LDS in one burst;
+// each wave keeps the scores of its key slice in registers, so its softmax
+// needs one exact row max and one exp2 pass, no online rescaling; its block
+// loops have wave-uniform trip counts. The KS slices of a query sub-block
+// are merged through LDS with the online-softmax combination (max, rescaled
+// sums), each wave finishing DV / KS of the value channels and storing them
+// straight to the pixel rows. KS = 4 (16 waves, four per SIMD, at most 128
+// VGPRs each) gives each SIMD more waves to hide latency with.
+template <int KD, int NB, int KS = 2>
 struct PsaSmallCfg {
     static constexpr int KC = 2 * NB * 32;       // key capacity (h*w <= KC)
+    static constexpr int NBS = (2 * NB + KS - 1) / KS;  // 32-key blocks per slice, at most
     // LDS rows hold KCL >= KC keys, a power of two, so that the loads map
     // threads to (row, 16-byte column) with shifts
     static constexpr int KCL = KC <= 64 ? 64 : KC <= 128 ? 128 : KC <= 256 ? 256 : 512;
     static constexpr int DV = 2 * KD;            // value width (V_lo | V_hi)
     static constexpr int BR = 128;               // queries per workgroup
+    static constexpr int NW = 4 * KS;            // waves
+    static constexpr int CPS = DV / KS;          // value channels each wave finishes
     // LDS strides (elements): transposed reads of K^T and Q^T want rows an
     // odd number of 64-byte units apart; V^T rows (8-byte reads down 32 rows)
     // KCL + 4 elements apart.
@@ -269,26 +289,30 @@ struct PsaSmallCfg {
     static constexpr int LDVT = KCL + 4;
     static constexpr int LDQ = BR + 32;
     static constexpr int KT_SZ = KD * LDKT, VT_SZ = DV * LDVT, QT_SZ = KD * LDQ;
-    // after the products the LDS holds the merge exchange (float)
-    static constexpr int XCH_FLOATS = 8 * 32 * (DV / 2 + 4) + 8 * 2 * 32;
+    // after the products the LDS holds the merge exchange (float): per wave
+    // and per other slice, 32 queries x CPS channels (+4 pad), then m and l
+    static constexpr int LDX = CPS + 4;
+    static constexpr int XCH_FLOATS = NW * (KS - 1) * 32 * LDX + NW * 2 * 32;
     static constexpr int MAIN_BYTES = 2 * (KT_SZ + VT_SZ + QT_SZ);
     static constexpr int LDS_BYTES = MAIN_BYTES > 4 * XCH_FLOATS ? MAIN_BYTES : 4 * XCH_FLOATS;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+    static_assert(CPS == 16 || CPS == 32 || CPS == 64, "channel slices of whole C-block halves");
 };
 
 // Largest map each key_dim handles with this kernel (32-key blocks per half).
 template <int KD> constexpr int psa_small_max_nb() { return KD == 32 ? 7 : 4; }
 
-template <Dt DT, int KD, int NB, bool ALIGNED>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void psa_small_kernel(
+template <Dt DT, int KD, int NB, bool ALIGNED, int KS = 2>
+__global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, KS))) void psa_small_kernel(
     const typename Traits<DT>::elem *__restrict__ qkv, typename Traits<DT>::elem *__restrict__ out,
     float *__restrict__ lse, int num_heads, int hw, int n_qblocks, int total_blocks, float scale_log2) {
     using Tr = Traits<DT>;
     using elem = typename Tr::elem;
     using frag = typename Tr::frag;
-    using C = PsaSmallCfg<KD, NB>;
+    using C = PsaSmallCfg<KD, NB, KS>;
     static_assert(Tr::KPL == 8, "16-bit element types");
-    constexpr int NT = 512, VEC = 8, TS = KD / 16, DV = C::DV, BR = C::BR, NDB = DV / 32;
+    constexpr int NT = 64 * C::NW, VEC = 8, TS = KD / 16, DV = C::DV, BR = C::BR, NDB = DV / 32;
+    constexpr int NBS = C::NBS;
     constexpr int LDKT = C::LDKT, LDVT = C::LDVT, LDQ = C::LDQ;
     __shared__ __attribute__((aligned(16))) unsigned char lds_raw[C::LDS_BYTES];
     elem *Kt = reinterpret_cast<elem *>(lds_raw);
@@ -297,7 +321,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int qs = wave & 3, ks = wave >> 2;  // waves w and w+4 share a SIMD
+    const int qs = wave & 3, ks = wave >> 2;  // waves w, w+4, ... share a SIMD
     const int h = lane >> 5, col = lane & 31;
     const int blk = xcd_remap(blockIdx.x, total_blocks);
     const int bh = blk / n_qblocks, qb = blk % n_qblocks;
@@ -314,9 +338,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // whole rows.
     constexpr int VPR = C::KCL / VEC, RPP = NT / VPR;
     constexpr int K_PER = (KD + RPP - 1) / RPP, V_PER = (DV + RPP - 1) / RPP;
-    constexpr int QPR = BR / VEC, Q_PER = KD * QPR / NT;  // Q^T: 16 vectors per row
+    constexpr int QPR = BR / VEC;                        // Q^T: 16 vectors per row
+    constexpr int QRP = NT / QPR;                        // Q^T rows per pass
+    constexpr int Q_PER = (KD + QRP - 1) / QRP;
     static_assert((KD % RPP == 0 || RPP % KD == 0) && (DV % RPP == 0 || RPP % DV == 0), "load mapping");
-    static_assert(KD * QPR == Q_PER * NT, "load mapping");
+    static_assert(KD % QRP == 0 || QRP % KD == 0, "load mapping");
     // buffer over the head's channel rows (Q, K, V_lo, V_hi are contiguous);
     // vectors past a row's hw pixels get an offset beyond the range and read
     // as zero
@@ -340,7 +366,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
     uint4 rq[Q_PER], rk[K_PER], rv[V_PER];
 #pragma unroll
-    for (int i = 0; i < Q_PER; ++i) rq[i] = load_vec(qr + (NT / QPR) * i, q0 + qc);
+    for (int i = 0; i < Q_PER; ++i)
+        if (KD % QRP == 0 || qr + QRP * i < KD) rq[i] = load_vec(qr + QRP * i, q0 + qc);
 #pragma unroll
     for (int i = 0; i < K_PER; ++i)
         if (KD % RPP == 0 || rbase + RPP * i < KD) rk[i] = load_vec(KD + rbase + RPP * i, pk);
@@ -348,7 +375,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int i = 0; i < V_PER; ++i)
         if (DV % RPP == 0 || rbase + RPP * i < DV) rv[i] = load_vec(2 * KD + rbase + RPP * i, pk);
 #pragma unroll
-    for (int i = 0; i < Q_PER; ++i) *reinterpret_cast<uint4 *>(Qt + (qr + (NT / QPR) * i) * LDQ + qc) = rq[i];
+    for (int i = 0; i < Q_PER; ++i)
+        if (KD % QRP == 0 || qr + QRP * i < KD) *reinterpret_cast<uint4 *>(Qt + (qr + QRP * i) * LDQ + qc) = rq[i];
 #pragma unroll
     for (int i = 0; i < K_PER; ++i)
         if (KD % RPP == 0 || rbase + RPP * i < KD)
@@ -364,23 +392,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
 
     // this wave: queries q0 + 32 qs + [0, 32), key blocks kb0 + [0, nb): the
-    // map's ceil(hw / 32) key blocks split evenly between the two halves
-    // (nb <= NB since hw <= 64 NB); blocks past nb are not computed
-    const int nblk = (hw + 31) / 32, nb_lo = (nblk + 1) / 2;
-    const int kb0 = ks ? nb_lo : 0;
-    const int nb = ks ? nblk - nb_lo : nb_lo;
+    // map's ceil(hw / 32) key blocks split evenly over the KS slices (the
+    // first nblk % KS slices take one more; nb <= NBS since hw <= 64 NB);
+    // blocks past nb are not computed
+    const int nblk = (hw + 31) / 32, nbase = nblk / KS, nrem = nblk % KS;
+    const int kb0 = ks * nbase + min(ks, nrem);
+    const int nb = nbase + (ks < nrem ? 1 : 0);
     const bool active = q0 + 32 * qs < hw && nb > 0;
     f32x16 acc[NDB];
 #pragma unroll
     for (int i = 0; i < NDB; ++i) acc[i] = zero16();
     float m = -INFINITY, l_run = 0.f;
-    f32x16 s[NB];
+    f32x16 s[NBS];
     if (active) {
         frag qf[TS];
 #pragma unroll
         for (int t = 0; t < TS; ++t) qf[t] = ld_vt_frag_tr<DT>(Qt, LDQ, 16 * t, 32 * qs, lane);
 #pragma unroll
-        for (int kb = 0; kb < NB; ++kb) {
+        for (int kb = 0; kb < NBS; ++kb) {
             if (kb >= nb) break;
             s[kb] = zero16();
 #pragma unroll
@@ -391,7 +420,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // past hw need the per-element test
         float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < NB; ++kb) {
+        for (int kb = 0; kb < NBS; ++kb) {
             if (kb >= nb) break;
             if (32 * (kb0 + kb + 1) > hw) {
                 const int limit = hw - 32 * (kb0 + kb) - 4 * h;  // first invalid crow - 4h
@@ -401,16 +430,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int c = 0; c < 16; ++c) mx = fmaxf(mx, s[kb][c]);
         }
-        m = xhalf_max(mx) * scale_log2;  // exact max of this half, log2 units
+        m = xhalf_max(mx) * scale_log2;  // exact max of this slice, log2 units
     }
     if (active) {
         // probabilities block by block, so that the exp2 of a block overlaps
         // the P V products of the one before; the row sum is taken over the
         // rounded probabilities the products use
-        // (a half with no keys keeps m = -inf and contributes nothing)
+        // (a slice with no keys keeps m = -inf and contributes nothing)
         const float neg_m = m == -INFINITY ? 0.f : -m;
 #pragma unroll
-        for (int kb = 0; kb < NB; ++kb) {
+        for (int kb = 0; kb < NBS; ++kb) {
             if (kb >= nb) break;
 #pragma unroll
             for (int c = 0; c < 16; ++c) s[kb][c] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][c], scale_log2, neg_m));
@@ -424,75 +453,122 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
         }
     }
-    const float l_half = xhalf_sum(l_run);
+    const float l_slice = xhalf_sum(l_run);
     __syncthreads();  // K^T / V^T no longer read: reuse the space
 
-    // Merge the two key halves. Wave (qs, ks) finishes channels
-    // [ks*DV/2, (ks+1)*DV/2) and hands the other half to its partner. The
-    // exchange is [wave][query][LDX] floats: a lane's registers 4g..4g+3 are
-    // 4 consecutive channels, moved as one 16-byte vector.
-    constexpr int LDX = DV / 2 + 4;
-    float *xch = reinterpret_cast<float *>(lds_raw);  // [wave][32][LDX]
-    float *ml = xch + 8 * 32 * LDX;                   // [wave][2][32]
-    constexpr int HDB = NDB / 2;                      // 32-channel blocks per half
-    {
-        const int give = 1 - ks;  // the half the partner finishes
-        float *dst = xch + (wave * 32 + col) * LDX;
+    // Merge the KS slices. Wave (qs, ks) finishes channels [ks CPS, (ks+1)
+    // CPS) and hands every other slice's channels to that slice's wave. A
+    // slice j covers registers [RL(j), RL(j) + RN) of C block j CPS / 32 (RN =
+    // 16 for whole blocks, 8 for half blocks: registers 8..15 hold channels
+    // 16..31 of the block in both lane halves); registers 4g..4g+3 are 4
+    // consecutive channels, moved as one 16-byte vector. Exchange layout:
+    // [source wave][other-slice index][query][LDX] floats, then m and l.
+    // NSB whole blocks per slice when CPS >= 32.
+    constexpr int CPS = C::CPS, LDX = C::LDX, RN = CPS >= 32 ? 16 : 8, NSB = CPS >= 32 ? CPS / 32 : 1;
+    float *xch = reinterpret_cast<float *>(lds_raw);
+    float *ml = xch + C::NW * (KS - 1) * 32 * LDX;  // [wave][2][32]
+    constexpr auto slice_db = [](int j) { return (j * CPS) / 32; };
+    constexpr auto slice_rl = [](int j) { return CPS >= 32 ? 0 : ((j * CPS) % 32) / 2; };
+    uniform_switch<KS>(ks, [&](auto ks_c) {
+        constexpr int KSV = decltype(ks_c)::value;
 #pragma unroll
-        for (int j = 0; j < HDB; ++j)
+        for (int j = 0; j < KS; ++j) {
+            if (j == KSV) continue;
+            const int jj = j < KSV ? j : j - 1;
+            float *dst = xch + ((wave * (KS - 1) + jj) * 32 + col) * LDX;
+            const int rl = slice_rl(j);
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x16 &a = acc[give * HDB + j];
-                *reinterpret_cast<float4 *>(dst + 32 * j + crow(4 * g, h)) =
-                    make_float4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
+            for (int sb = 0; sb < NSB; ++sb) {
+                const f32x16 &a = acc[slice_db(j) + sb];
+#pragma unroll
+                for (int g = 0; g < RN / 4; ++g) {
+                    const int c = rl + 4 * g;
+                    *reinterpret_cast<float4 *>(dst + 32 * sb + crow(c, h) - 2 * rl) =
+                        make_float4(a[c], a[c + 1], a[c + 2], a[c + 3]);
+                }
             }
-        if (h == 0) {
-            ml[wave * 64 + col] = m;
-            ml[wave * 64 + 32 + col] = l_half;
         }
+    });
+    if (h == 0) {
+        ml[wave * 64 + col] = m;
+        ml[wave * 64 + 32 + col] = l_slice;
     }
     __syncthreads();
-    const int partner = wave ^ 4;
-    const float m_o = ml[partner * 64 + col], l_o = ml[partner * 64 + 32 + col];
-    const float m_max = fmaxf(m, m_o);
-    const float a_s = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_max);
-    const float a_o = m_o == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_o - m_max);
-    const float l_tot = l_half * a_s + l_o * a_o;
+    float mj[KS], lj[KS];
+    float m_max = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+        const int w = qs + 4 * j;
+        mj[j] = ml[w * 64 + col];
+        lj[j] = ml[w * 64 + 32 + col];
+        m_max = fmaxf(m_max, mj[j]);
+    }
+    float aj[KS];
+    float l_tot = 0.f;
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+        aj[j] = mj[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mj[j] - m_max);
+        l_tot += lj[j] * aj[j];
+    }
     const float inv = 1.f / l_tot;
     const int qrow = q0 + 32 * qs + col;
     if (lse != nullptr && ks == 0 && h == 0 && qrow < hw) lse[(int64_t)bh * hw + qrow] = (m_max + __log2f(l_tot)) * kLn2;
-    if (qrow < hw) {
-        // channel 32 (ks HDB + j) + crow(c, h), pixel qrow: each store
-        // instruction writes 32 consecutive pixels of two channel rows
-        const float *src = xch + (partner * 32 + col) * LDX;
+    if (qrow < hw) uniform_switch<KS>(ks, [&](auto ks_c) {
+        // channel 32 db + crow(c, h), pixel qrow: each store instruction
+        // writes 32 consecutive pixels of two channel rows
+        constexpr int KSV = decltype(ks_c)::value;
+        constexpr int rl = slice_rl(KSV);
 #pragma unroll
-        for (int j = 0; j < HDB; ++j)
+        for (int sb = 0; sb < NSB; ++sb) {
+            const int db = slice_db(KSV) + sb;
+            const f32x16 &a = acc[db];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const float4 x = *reinterpret_cast<const float4 *>(src + 32 * j + crow(4 * g, h));
-                const f32x16 &a = acc[ks * HDB + j];
-                const float xo[4] = {x.x, x.y, x.z, x.w};
+            for (int g = 0; g < RN / 4; ++g) {
+                const int c = rl + 4 * g;
+                float v[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = 0.f;
+#pragma unroll
+                for (int j = 0; j < KS; ++j) {
+                    float x[4];
+                    if (j == KSV) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) x[i] = a[c + i];
+                    } else {
+                        const int jj = KSV < j ? KSV : KSV - 1;  // this slice's index in wave j's list
+                        const float *src = xch + (((qs + 4 * j) * (KS - 1) + jj) * 32 + col) * LDX;
+                        const float4 y = *reinterpret_cast<const float4 *>(src + 32 * sb + crow(c, h) - 2 * rl);
+                        x[0] = y.x;
+                        x[1] = y.y;
+                        x[2] = y.z;
+                        x[3] = y.w;
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] += x[i] * aj[j];
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int chn = 32 * (ks * HDB + j) + crow(4 * g + i, h);
-                    obase[(int64_t)chn * plane + qrow] = static_cast<elem>((a[4 * g + i] * a_s + xo[i] * a_o) * inv);
+                    const int chn = 32 * db + crow(c + i, h);
+                    obase[(int64_t)chn * plane + qrow] = static_cast<elem>(v[i] * inv);
                 }
             }
-    }
+        }
+    });
 }
 
-template <Dt DT, int KD, int NB>
+template <Dt DT, int KD, int NB, int KS = 2>
 static hipError_t psa_small_launch(const void *qkv, void *out, float *lse, const PsaShape &s, hipStream_t stream) {
     using elem = typename Traits<DT>::elem;
-    constexpr int BR = PsaSmallCfg<KD, NB>::BR;
+    constexpr int BR = PsaSmallCfg<KD, NB, KS>::BR;
+    constexpr int NT = 64 * PsaSmallCfg<KD, NB, KS>::NW;
     const int nqb = (s.hw + BR - 1) / BR;
     const int grid = s.batch * s.num_heads * nqb;
     const float scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)KD));
     if (s.hw % 8 == 0)
-        hipLaunchKernelGGL((psa_small_kernel<DT, KD, NB, true>), dim3(grid), dim3(512), 0, stream,
+        hipLaunchKernelGGL((psa_small_kernel<DT, KD, NB, true, KS>), dim3(grid), dim3(NT), 0, stream,
                            (const elem *)qkv, (elem *)out, lse, s.num_heads, s.hw, nqb, grid, scale_log2);
     else
-        hipLaunchKernelGGL((psa_small_kernel<DT, KD, NB, false>), dim3(grid), dim3(512), 0, stream,
+        hipLaunchKernelGGL((psa_small_kernel<DT, KD, NB, false, KS>), dim3(grid), dim3(NT), 0, stream,
                            (const elem *)qkv, (elem *)out, lse, s.num_heads, s.hw, nqb, grid, scale_log2);
     return hipGetLastError();
 }
