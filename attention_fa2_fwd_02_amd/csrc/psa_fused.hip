@@ -263,7 +263,9 @@ __device__ __forceinline__ void uniform_switch(int v, F &&f) {
 // of 32 x KS key slices (the map's ceil(h*w / 32) blocks of 32 keys split
 // evenly; a ragged last block is masked). Wave w runs on SIMD w % 4, so the
 // KS slices of one query sub-block share a SIMD. The head's whole K^T and
-// V^T (zero past h*w) and the Q^T block are fetched into LDS in one burst;
+// V^T (zero past h*w) and the Q^T block are fetched in one burst of loads;
+// Q^T and K^T are written to LDS first and the score products start while
+// V^T is still arriving;
 // each wave keeps the scores of its key slice in registers, so its softmax
 // needs one exact row max and one exp2 pass, no online rescaling; its block
 // loops have wave-uniform trip counts. The KS slices of a query sub-block
@@ -381,14 +383,6 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, KS
     for (int i = 0; i < K_PER; ++i)
         if (KD % RPP == 0 || rbase + RPP * i < KD)
             *reinterpret_cast<uint4 *>(Kt + (rbase + RPP * i) * LDKT + pk) = rk[i];
-#pragma unroll
-    for (int i = 0; i < V_PER; ++i) {
-        if (DV % RPP == 0 || rbase + RPP * i < DV) {  // V^T rows are 8-byte aligned
-            elem *dst = Vt + (rbase + RPP * i) * LDVT + pk;
-            reinterpret_cast<uint2 *>(dst)[0] = make_uint2(rv[i].x, rv[i].y);
-            reinterpret_cast<uint2 *>(dst)[1] = make_uint2(rv[i].z, rv[i].w);
-        }
-    }
     __syncthreads();
 
     // this wave: queries q0 + 32 qs + [0, 32), key blocks kb0 + [0, nb): the
@@ -432,6 +426,18 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, KS
         }
         m = xhalf_max(mx) * scale_log2;  // exact max of this slice, log2 units
     }
+    // V^T (two thirds of the loaded bytes) goes to LDS only now: its loads
+    // were issued with those of Q and K, and stream in during the products
+    // above
+#pragma unroll
+    for (int i = 0; i < V_PER; ++i) {
+        if (DV % RPP == 0 || rbase + RPP * i < DV) {  // V^T rows are 8-byte aligned
+            elem *dst = Vt + (rbase + RPP * i) * LDVT + pk;
+            reinterpret_cast<uint2 *>(dst)[0] = make_uint2(rv[i].x, rv[i].y);
+            reinterpret_cast<uint2 *>(dst)[1] = make_uint2(rv[i].z, rv[i].w);
+        }
+    }
+    __syncthreads();
     if (active) {
         // probabilities block by block, so that the exp2 of a block overlaps
         // the P V products of the one before; the row sum is taken over the
