@@ -68,13 +68,17 @@ constexpr int fwd_ldv() {
 // One key tile of the forward for one wave: scores, online softmax with lazy
 // rescaling, and the P V accumulation. MASK: the tile is the ragged last one
 // and keys at or beyond kvalid do not exist (probability 0). FAST: the row
-// max is taken only when `first` (wave-uniform) is set; otherwise the
-// probabilities use the current reference as they are (see fwd_kernel).
-template <Dt DT, int D, int BC, bool MASK, bool FAST = false>
+// max is taken only on the FIRST tile; later tiles use the current reference
+// as it is (see fwd_kernel). FIRST is a template parameter so that the
+// steady-state loop body has no branch between the score products and the
+// softmax: the exponentials of the first key block can then be scheduled
+// among the products of the second (5% faster at head_dim 64, the same at
+// 128).
+template <Dt DT, int D, int BC, bool MASK, bool FAST = false, bool FIRST = true>
 __device__ __forceinline__ void fwd_tile(const typename Traits<DT>::elem *kt, const typename Traits<DT>::elem *vt,
                                          const typename Traits<DT>::frag (&qf)[D / (2 * Traits<DT>::KPL)],
                                          f32x16 (&acc)[D / 32], float &m_ref, float &l_run, float scale_log2,
-                                         int kvalid, int lane, bool first = true) {
+                                         int kvalid, int lane) {
     using Tr = Traits<DT>;
     using elem = typename Tr::elem;
     using frag = typename Tr::frag;
@@ -89,16 +93,26 @@ __device__ __forceinline__ void fwd_tile(const typename Traits<DT>::elem *kt, co
     constexpr int TS = D / KSTEP;
     constexpr int TP = 32 / KSTEP;
     const int h = lane >> 5, col = lane & 31;
-    // S^T = K Q^T (raw dot products), one 32x32 block per 32 keys; the
-    // two blocks' accumulation chains are interleaved.
+    // S^T = K Q^T (raw dot products), one 32x32 block per 32 keys. 16-bit
+    // types: block by block, so the first block is complete while the
+    // second's products still run; float32: the blocks' chains interleaved
+    // (the layout its tests verify).
     f32x16 s[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) s[kb] = zero16();
-#pragma unroll
-    for (int t = 0; t < TS; ++t)
+    if constexpr (TR) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
-            s[kb] = Tr::mfma(ld_row_frag<DT>(kt + (32 * kb + col) * LDK, t, h), qf[t], s[kb]);
+#pragma unroll
+            for (int t = 0; t < TS; ++t)
+                s[kb] = Tr::mfma(ld_row_frag<DT>(kt + (32 * kb + col) * LDK, t, h), qf[t], s[kb]);
+    } else {
+#pragma unroll
+        for (int t = 0; t < TS; ++t)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+                s[kb] = Tr::mfma(ld_row_frag<DT>(kt + (32 * kb + col) * LDK, t, h), qf[t], s[kb]);
+    }
 
     // ragged last tile: keys >= kvalid do not exist (probability 0)
     if constexpr (MASK) {
@@ -108,7 +122,7 @@ __device__ __forceinline__ void fwd_tile(const typename Traits<DT>::elem *kt, co
             for (int c = 0; c < 16; ++c)
                 if (32 * kb + crow(c, h) >= kvalid) s[kb][c] = -INFINITY;
     }
-    if (!FAST || first) {
+    if constexpr (!FAST || FIRST) {
         // lane-partial max of the raw scores (scale > 0, so the max commutes
         // with scaling)
         float mx = -INFINITY;
@@ -286,9 +300,22 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
             vload(BC);
         }
         __syncthreads();
-        for (int it = 0; it < nfull; ++it) {
-            fwd_tile<DT, D, BC, false, FASTP>(Ks + (it & 1) * KS, Vs + (it & 1) * VS, qf, acc, m_ref, l_run,
-                                              scale_log2, BC, lane, it == 0);
+        // 16-bit types: the first tile peeled off (FIRST is a template
+        // parameter); float32 keeps one loop over all full tiles (its exact
+        // pass takes the max on every tile either way; the peeled layout
+        // gave wrong outputs for float32 at head_dim 64 with 4 waves, like
+        // the two-pass form below)
+        int it0 = 0;
+        if constexpr (TR) {
+            if (nfull > 0) {
+                fwd_tile<DT, D, BC, false, FASTP, true>(Ks, Vs, qf, acc, m_ref, l_run, scale_log2, BC, lane);
+                advance(0);
+                it0 = 1;
+            }
+        }
+        for (int it = it0; it < nfull; ++it) {
+            fwd_tile<DT, D, BC, false, FASTP, !TR>(Ks + (it & 1) * KS, Vs + (it & 1) * VS, qf, acc, m_ref, l_run,
+                                                   scale_log2, BC, lane);
             advance(it);
         }
         if (nfull < ntiles)
