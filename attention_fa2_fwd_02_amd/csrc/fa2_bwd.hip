@@ -245,10 +245,20 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             f32x16 s = zero16(), dp = zero16();
+            if constexpr (TR) {
+                // 16-bit types: the S chain first, so that its exponentials
+                // can be scheduled among the dP products (1% faster at the
+                // LLM shape, same results)
 #pragma unroll
-            for (int t = 0; t < TS; ++t) {
-                s = Tr::mfma(Tl::row(kt, 32 * kb + col, t, h), qf[t], s);
-                dp = Tr::mfma(Tl::row(vt, 32 * kb + col, t, h), df[t], dp);
+                for (int t = 0; t < TS; ++t) s = Tr::mfma(Tl::row(kt, 32 * kb + col, t, h), qf[t], s);
+#pragma unroll
+                for (int t = 0; t < TS; ++t) dp = Tr::mfma(Tl::row(vt, 32 * kb + col, t, h), df[t], dp);
+            } else {
+#pragma unroll
+                for (int t = 0; t < TS; ++t) {
+                    s = Tr::mfma(Tl::row(kt, 32 * kb + col, t, h), qf[t], s);
+                    dp = Tr::mfma(Tl::row(vt, 32 * kb + col, t, h), df[t], dp);
+                }
             }
 #pragma unroll
             for (int c = 0; c < 16; ++c) {
