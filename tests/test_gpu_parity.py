@@ -50,7 +50,10 @@ def _inputs(dt, bh, nq, nk, d, seed, k_mult=1.0, with_do=False):
     return workloads.attn_inputs(w, device=DEV, with_do=with_do)
 
 
-FWD_SHAPES = [(2, 64, 64), (3, 200, 333), (2, 1, 1), (1, 129, 65), (2, 400, 400), (1, 7, 300), (1, 300, 7)]
+# n_k 64 and 128: one and two full key tiles with no ragged tail (the first tile
+# runs outside the tile loop); 1 and 7: no full tile
+FWD_SHAPES = [(2, 64, 64), (3, 200, 333), (2, 1, 1), (1, 129, 65), (2, 400, 400), (1, 7, 300), (1, 300, 7),
+              (2, 96, 128)]
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
