@@ -36,6 +36,9 @@ fa2_status check_attn(const char *fn, fa2_dtype dt, int64_t bh, int64_t n_q, int
     if (bh <= 0 || n_q <= 0 || n_k <= 0 || head_dim <= 0)
         return fail(FA2_ERR_INVALID_ARG, fn, "bh, n_q, n_k and head_dim must all be > 0");
     if (!good_dim(head_dim)) return fail(FA2_ERR_UNSUPPORTED, fn, "head_dim must be 32, 64 or 128");
+    // the kernels take the lengths as int; bounding them first also keeps
+    // the byte count below within int64
+    if (n_q > INT_MAX || n_k > INT_MAX) return fail(FA2_ERR_INVALID_ARG, fn, "n_q and n_k must be below 2^31");
     // One head's [n, head_dim] rows stay within 2 GiB, so the kernels' 32-bit
     // byte offsets (including a tile read past the last row) cannot wrap.
     const int64_t es = dt == FA2_F32 ? 4 : 2;

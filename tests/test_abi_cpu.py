@@ -60,6 +60,8 @@ def _fwd(**kw):
     ({"n_k": (1 << 23) + 1, "d": 128}, INVALID),    # bf16 keys: 2 GiB + 256 B
     ({"dt": 0, "n_q": (1 << 22) + 1, "d": 128}, INVALID),  # f32: 2 GiB + 512 B
     ({"bh": 1 << 40, "n_q": 1 << 20}, INVALID),     # grid over 2^31-1 workgroups
+    ({"n_q": 1 << 60}, INVALID),                    # length beyond int (its byte count would overflow int64)
+    ({"n_k": (1 << 62) + 1}, INVALID),
 ])
 def test_fwd_rejects_invalid_arguments(kw, code):
     assert _fwd(**kw) == code
