@@ -275,6 +275,36 @@ def _time_batch(torch, fn, calls, warm=3):
     return s.elapsed_time(e) / calls
 
 
+def _time_graph(torch, fn, calls, reps=5):
+    """Average time per call of `calls` calls captured in one HIP graph,
+    median over `reps` replays (launch work done at capture, as in a
+    graph-captured serving loop)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        g.replay()
+        e.record()
+        torch.cuda.synchronize()
+        ts.append(s.elapsed_time(e) / calls)
+    ts.sort()
+    del g
+    return ts[len(ts) // 2]
+
+
 def _legs(torch, fa2, workloads, dev, only=None):
     legs = {}
     if only in (None, "c3_fwd"):
@@ -411,6 +441,7 @@ def _leg_c2(torch, fa2, workloads, dev, legs):
     del flush
     fused_bytes = byts["fused"]  # qkv read once, out written once
     fused_stream = _time_batch(torch, lambda: fa2.psa_attn_fused(qkv, w2.num_heads, w2.key_dim, out_f), 200)
+    fused_graph = _time_graph(torch, lambda: fa2.psa_attn_fused(qkv, w2.num_heads, w2.key_dim, out_f), 100)
     block_stream = _time_batch(torch, lambda: fa2.psa_block(qkv, w2.num_heads, w2.key_dim, ws), 200)
     # backward of the block (merge backward, attention backward of both
     # calls, pack backward) from the forward's workspace
@@ -433,6 +464,7 @@ def _leg_c2(torch, fa2, workloads, dev, legs):
     fbwd_stream = _time_batch(torch, fbwd, 200)
     legs["c2"] = {
         "fused_us_per_call_stream": round(fused_stream * 1e3, 2),
+        "fused_us_per_call_graph": round(fused_graph * 1e3, 2),
         "block_us_per_call_stream": round(block_stream * 1e3, 2),
         "fused_gbs_stream": round(fused_bytes / (fused_stream * 1e-3) / 1e9, 1),
         "fused_us_per_call_warm": round(fused_warm * 1e3, 2), "fused_us_per_call_cold": round(fused_cold * 1e3, 2),
