@@ -50,7 +50,7 @@ def _parse():
     ap.add_argument("--no-legs", action="store_true", help="skip the other-shape legs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0, help="oracle sample heads (0: three per thread)")
-    ap.add_argument("--only", choices=["main", "c3_fwd", "c4", "c5", "c2", "decode", "gemm_ref"], default=None,
+    ap.add_argument("--only", choices=["main", "c3_fwd", "c4", "c5", "c2", "decode", "gemm_ref", "vendor_ref"], default=None,
                     help="run just the main step or just one leg (for profiling one workload); prints no JSON "
                          "line unless it is the main step")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -319,7 +319,78 @@ def _legs(torch, fa2, workloads, dev, only=None):
         _leg_decode(torch, fa2, workloads, dev, legs)
     if only in (None, "gemm_ref"):
         _leg_gemm_ref(torch, dev, legs)
+    if only == "vendor_ref":  # not in the default run: times a third-party kernel
+        _leg_vendor_ref(torch, fa2, workloads, dev, legs)
     return legs
+
+
+def _leg_vendor_ref(torch, fa2, workloads, dev, legs):
+    """torch's scaled_dot_product_attention with its flash backend forced (no
+    fallback to the composed math path) beside this library, same inputs:
+    the C3 and C4 forwards and the C5 backward (autograd through the flash
+    backward, timed from the saved forward). Reference context only."""
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    def timed(fn, reps=6):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn()
+            e.record()
+            torch.cuda.synchronize()
+            ts.append(s.elapsed_time(e))
+        ts.sort()
+        return ts[len(ts) // 2]
+
+    def sdpa(q, k, v):
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            return torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=None)
+
+    out = {}
+    try:
+        for name, w, heads in (("c3_fwd", workloads.C3, 32), ("c4_fwd", workloads.C4, 16)):
+            x = workloads.attn_inputs(w, device=dev)
+            b = w.bh // heads
+            q4, k4, v4 = (x[t].view(b, heads, -1, w.head_dim) for t in ("q", "k", "v"))
+            o_v = sdpa(q4, k4, v4)
+            o, lse = fa2.fa2_fwd(x["q"], x["k"], x["v"], w.scale)
+            torch.cuda.synchronize()
+            diff = (o_v.reshape(o.shape).float() - o.float()).abs().max().item()
+            del o_v
+            tv = timed(lambda: sdpa(q4, k4, v4))
+            to = timed(lambda: fa2.fa2_fwd(x["q"], x["k"], x["v"], w.scale, o, lse))
+            fl = w.fwd_flops()
+            out[name] = {"vendor_ms": round(tv, 4), "vendor_tflops": round(fl / tv / 1e9, 1), "ours_ms": round(to, 4),
+                         "ours_tflops": round(fl / to / 1e9, 1), "max_abs_diff_o": diff}
+            del x, q4, k4, v4, o, lse
+            torch.cuda.empty_cache()
+        w = workloads.C5
+        x = workloads.attn_inputs(w, device=dev)
+        heads = 32
+        q4, k4, v4, do4 = (x[t].view(w.bh // heads, heads, w.n_q, w.head_dim) for t in ("q", "k", "v", "do"))
+        qr, kr, vr = (t.clone().requires_grad_(True) for t in (q4, k4, v4))
+        o_v = sdpa(qr, kr, vr)
+        o, lse = fa2.fa2_fwd(x["q"], x["k"], x["v"], w.scale)
+        grads = torch.autograd.grad(o_v, (qr, kr, vr), do4, retain_graph=True)
+        ours = fa2.attention_bwd(x["q"], x["k"], x["v"], o, x["do"], lse, w.scale)
+        torch.cuda.synchronize()
+        diff = max((g.reshape(m.shape).float() - m.float()).abs().max().item() for g, m in zip(grads, ours))
+        del grads, ours
+        tv = timed(lambda: torch.autograd.grad(o_v, (qr, kr, vr), do4, retain_graph=True))
+        to = timed(lambda: fa2.attention_bwd(x["q"], x["k"], x["v"], o, x["do"], lse, w.scale))
+        fl = w.bwd_flops()
+        out["c5_bwd"] = {"vendor_ms": round(tv, 4), "vendor_tflops_counted": round(fl / tv / 1e9, 1),
+                         "ours_ms": round(to, 4), "ours_tflops_counted": round(fl / to / 1e9, 1),
+                         "max_abs_diff_grads": diff}
+        del x, q4, k4, v4, do4, qr, kr, vr, o_v, o, lse
+        torch.cuda.empty_cache()
+    except RuntimeError as e:  # the flash backend is not available on this build
+        out["error"] = str(e)[:200]
+    legs["vendor_ref"] = out
+    print(f"[bench] leg vendor_ref {out}", file=sys.stderr, flush=True)
 
 
 def _leg_decode(torch, fa2, workloads, dev, legs):
