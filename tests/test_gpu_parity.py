@@ -421,6 +421,29 @@ def test_bwd_small(dt, d, shape):
         _err(name, _np(got), want, tol, case)
 
 
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("shape", [(256, 100, 150), (512, 90, 130), (64, 300, 520)],
+                         ids=["4waves", "8waves", "2waves-multi"])
+def test_bwd_workgroup_sizes(dt, d, shape):
+    """Shapes whose head count selects 4-wave (128-row) and 8-wave (256-row)
+    workgroups in both dq (query rows) and dkdv (key rows), and a 2-wave
+    launch with several query and key tiles per workgroup; every dQ, dK and
+    dV element against the oracle (the small shapes above run 2-wave
+    workgroups with one or two tiles)."""
+    bh, nq, nk = shape
+    case = f"bwd {dt} d={d} bh={bh} nq={nq} nk={nk}"
+    print(case, flush=True)
+    x = _inputs(dt, bh, nq, nk, d, seed=600 + bh + d, with_do=True)
+    o, lse = fa2.fa2_fwd(x["q"], x["k"], x["v"])
+    dq, dk, dv = fa2.attention_bwd(x["q"], x["k"], x["v"], o, x["do"], lse)
+    torch.cuda.synchronize()
+    ref = oracle.attention_bwd(x["q"], x["k"], x["v"], x["do"], 1 / math.sqrt(d))
+    tol = TOL[DTYPES[dt]]
+    for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        _err(name, _np(got), want, tol, case)
+
+
 def test_bwd_delta_matches_rowsum():
     x = _inputs("bf16", 3, 130, 10, 128, seed=12, with_do=True)
     o = x["v"].new_empty(0)
@@ -572,7 +595,11 @@ def test_bwd_long_keys():
                                          (32, 1, 1, 1, 1), (64, 3, 1, 16, 24), (32, 2, 2, 13, 11),
                                          # whole-head kernel capacity (448 / 256 pixels) and one past it
                                          (32, 1, 2, 16, 28), (32, 1, 1, 1, 449),
-                                         (64, 1, 2, 16, 16), (64, 1, 1, 1, 257)])
+                                         (64, 1, 2, 16, 16), (64, 1, 1, 1, 257),
+                                         # tiled kernel with 16-byte vector access (h*w % 8 == 0)
+                                         (32, 1, 1, 16, 32), (64, 1, 2, 16, 24),
+                                         # tiled kernel, 4-wave launch (many workgroups), aligned and not
+                                         (32, 64, 4, 16, 32), (64, 64, 4, 15, 35)])
 def test_psa_attn_fused(dt, kd, b, nh, h, w):
     dtype = DTYPES[dt]
     case = f"psa fused {dt} kd={kd} b={b} nh={nh} h={h} w={w}"
