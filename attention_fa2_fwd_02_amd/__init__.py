@@ -10,7 +10,8 @@ every function raises if the library is missing or the tensors are not on a
 GPU.
 
 Entry points (same names as the C ABI):
-  fa2_fwd, fa2_fwd_splitkv_plan, fa2_fwd_splitkv, fa2_pad_cols, fa2_bwd_delta,
+  fa2_fwd, fa2_fwd_splitkv_plan, fa2_fwd_splitkv, fa2_fwd_splitkv_noalloc,
+  fa2_fwd_splitkv_noalloc_max_bytes, fa2_pad_cols, fa2_bwd_delta,
   fa2_bwd_dq, fa2_bwd_dkdv, psa_pack_qkv, psa_merge_attn, psa_attn_fused,
   psa_attn_fused_backward, psa_merge_attn_backward, psa_pack_qkv_backward,
   psa_extract_v_nchw, psa_extract_v_backward
@@ -33,7 +34,8 @@ from . import _lib
 from ._lib import FA2_BF16, FA2_F16, FA2_F32, Fa2Error, library_path, load  # noqa: F401
 
 __all__ = [
-    "fa2_fwd", "fa2_fwd_splitkv_plan", "fa2_fwd_splitkv", "fa2_pad_cols", "fa2_bwd_delta", "fa2_bwd_dq",
+    "fa2_fwd", "fa2_fwd_splitkv_plan", "fa2_fwd_splitkv", "fa2_fwd_splitkv_noalloc",
+    "fa2_fwd_splitkv_noalloc_max_bytes", "fa2_pad_cols", "fa2_bwd_delta", "fa2_bwd_dq",
     "fa2_bwd_dkdv", "psa_pack_qkv", "psa_merge_attn", "psa_attn_fused", "psa_attn_fused_backward",
     "psa_merge_attn_backward", "psa_pack_qkv_backward", "psa_extract_v_nchw", "psa_extract_v_backward",
     "attention_fwd", "attention_bwd", "psa_block", "psa_block_backward", "Fa2Error", "load", "library_path",
@@ -133,6 +135,29 @@ def fa2_fwd_splitkv(q, k, v, scale=None, num_splits=0, workspace=None, o=None, l
     _lib.call("fa2_fwd_splitkv", _dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
               lse.data_ptr(), workspace.data_ptr(), workspace.numel(), bh, n_q, n_k, d, _scale(scale, d),
               num_splits, _stream(dev))
+    return o, lse
+
+
+def fa2_fwd_splitkv_noalloc_max_bytes() -> int:
+    """Size in bytes of the static device scratch of fa2_fwd_splitkv_noalloc."""
+    return int(load().fa2_fwd_splitkv_noalloc_max_bytes())
+
+
+def fa2_fwd_splitkv_noalloc(q, k, v, o, lse, scale=None, num_splits=0):
+    """Key-split forward into caller-provided o and lse with the library's
+    static device scratch in place of a workspace (no device allocation in
+    the call). Calls overlapping on one device share that scratch and race:
+    keep them on one stream. Partials larger than the scratch raise Fa2Error."""
+    _check("q", q)
+    bh, n_q, d = q.shape
+    n_k = k.shape[1]
+    dev = q.device
+    _check("k", k, q.dtype, (bh, n_k, d), dev)
+    _check("v", v, q.dtype, (bh, n_k, d), dev)
+    _check("o", o, q.dtype, q.shape, dev)
+    _check("lse", lse, torch.float32, (bh, n_q), dev)
+    _lib.call("fa2_fwd_splitkv_noalloc", _dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+              lse.data_ptr(), bh, n_q, n_k, d, _scale(scale, d), num_splits, _stream(dev))
     return o, lse
 
 

@@ -24,6 +24,8 @@ SIGNATURES = {
     "fa2_fwd": [_int, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i32, _f32, _p],
     "fa2_fwd_splitkv_plan": [_int, _i64, _i64, _i64, _i32, _i32, _p, _p],
     "fa2_fwd_splitkv": [_int, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _f32, _i32, _p],
+    "fa2_fwd_splitkv_noalloc_max_bytes": [],
+    "fa2_fwd_splitkv_noalloc": [_int, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i32, _f32, _i32, _p],
     "fa2_bwd_delta": [_int, _p, _p, _p, _i64, _i64, _i32, _p],
     "fa2_bwd_dq": [_int, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i32, _f32, _p],
     "fa2_bwd_dkdv": [_int, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i32, _f32, _p],
@@ -37,7 +39,8 @@ SIGNATURES = {
     "psa_extract_v_nchw": [_int, _p, _p, _i32, _i32, _i32, _i32, _i32, _p],
     "psa_extract_v_backward": [_int, _p, _p, _i32, _i32, _i32, _i32, _i32, _p],
 }
-_RESTYPES = {"fa2_abi_version": _i32, "fa2_status_str": ctypes.c_char_p, "fa2_last_error": ctypes.c_char_p}
+_RESTYPES = {"fa2_abi_version": _i32, "fa2_fwd_splitkv_noalloc_max_bytes": _i64,
+             "fa2_status_str": ctypes.c_char_p, "fa2_last_error": ctypes.c_char_p}
 
 
 class Fa2Error(RuntimeError):

@@ -1,9 +1,11 @@
 // C ABI of libfa2mi: argument validation, then one launch on the caller's
 // stream. Validation never touches the HIP runtime, so a rejected call has no
 // side effect at all.
+#include <atomic>
 #include <climits>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/fa2mi.h"
 #include "fa2_launch.h"
@@ -70,6 +72,40 @@ fa2_status check_psa(const char *fn, fa2_dtype dt, int32_t batch, int32_t num_he
     const int64_t tiles = (int64_t)batch * num_heads * 4 * ((hw + 7) / 8);
     if (tiles > INT_MAX) return fail(FA2_ERR_INVALID_ARG, fn, "grid exceeds 2^31 - 1 workgroups");
     return FA2_OK;
+}
+
+}  // namespace
+
+// Scratch of the allocation-free key-split forward: the float32 partial
+// outputs and log2-sum-exps that fa2_fwd_splitkv keeps in a caller workspace.
+// Every device the library runs on holds its own copy from the time the code
+// object is loaded until the process ends. In host code `scratch` only names
+// the symbol: its device address on the current device comes from
+// hipGetSymbolAddress (taken once per device, then cached).
+constexpr int64_t kNoAllocScratchBytes = int64_t(32) << 20;
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on device `dev`, which must be current.
+hipError_t scratch_ptr(int dev, void **out) {
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (p == nullptr) return hipErrorInvalidSymbol;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
 }
 
 }  // namespace
@@ -176,6 +212,46 @@ fa2_status fa2_fwd_splitkv(fa2_dtype dt, const void *q, const void *k, const voi
     }
     const fa2mi::AttnShape s{bh, (int)n_q, (int)n_k, head_dim, scale};
     return launched(fn, fa2mi::launch_fwd_splitkv((int)dt, q, k, v, o, lse, static_cast<float *>(workspace), s, p,
+                                                  (hipStream_t)stream));
+}
+
+int64_t fa2_fwd_splitkv_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+fa2_status fa2_fwd_splitkv_noalloc(fa2_dtype dt, const void *q, const void *k, const void *v, void *o, float *lse,
+                                   int64_t bh, int64_t n_q, int64_t n_k, int32_t head_dim, float scale,
+                                   int32_t num_splits, void *stream) {
+    static const char fn[] = "fa2_fwd_splitkv_noalloc";
+    fa2_status st = check_attn(fn, dt, bh, n_q, n_k, head_dim, scale, fa2mi::kFwdRowsPerBlock, n_q);
+    if (st != FA2_OK) return st;
+    if (num_splits < 0) return fail(FA2_ERR_INVALID_ARG, fn, "num_splits must be >= 0 (0 picks it)");
+    REQUIRE_PTR(fn, q);
+    REQUIRE_PTR(fn, k);
+    REQUIRE_PTR(fn, v);
+    REQUIRE_PTR(fn, o);
+    REQUIRE_PTR(fn, lse);
+    const fa2mi::SplitPlan p = fa2mi::plan_splitkv(bh, n_q, n_k, head_dim, num_splits);
+    if (p.ws_bytes < 0) return fail(FA2_ERR_INVALID_ARG, fn, "grid exceeds 2^31 - 1 workgroups");
+    if (p.ws_bytes > kNoAllocScratchBytes)
+        return fail(FA2_ERR_INVALID_ARG, fn,
+                    "partials exceed the 32 MiB static scratch (splits * bh * n_q * (head_dim + 1) * 4 bytes); "
+                    "use fa2_fwd_splitkv with a workspace");
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(FA2_ERR_LAUNCH, fn, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(FA2_ERR_UNSUPPORTED, fn, "device index above 63");
+    if (stream != nullptr) {
+        int sdev = -1;
+        e = hipStreamGetDevice((hipStream_t)stream, &sdev);
+        if (e != hipSuccess) return fail(FA2_ERR_INVALID_ARG, fn, hipGetErrorString(e));
+        if (sdev != dev) return fail(FA2_ERR_INVALID_ARG, fn, "stream does not belong to the current device");
+    }
+    void *ws = nullptr;
+    if (p.ws_bytes > 0) {
+        e = scratch_ptr(dev, &ws);
+        if (e != hipSuccess) return fail(FA2_ERR_LAUNCH, fn, hipGetErrorString(e));
+    }
+    const fa2mi::AttnShape s{bh, (int)n_q, (int)n_k, head_dim, scale};
+    return launched(fn, fa2mi::launch_fwd_splitkv((int)dt, q, k, v, o, lse, static_cast<float *>(ws), s, p,
                                                   (hipStream_t)stream));
 }
 

@@ -118,6 +118,29 @@ fa2_status fa2_fwd_splitkv(fa2_dtype dt, const void *q, const void *k, const voi
                            int32_t num_splits, void *stream);
 
 /*
+ * Allocation-free key-split forward, for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops that forbid
+ * allocation). Same arguments and results as fa2_fwd_splitkv without the
+ * workspace: the float32 partials live in a static device array of
+ * fa2_fwd_splitkv_noalloc_max_bytes() bytes (32 MiB) that the library holds
+ * on every device it runs on until the process ends. Calls nothing that
+ * allocates. The partials are fully written before they are read, so the
+ * array needs no clearing and its contents between calls do not matter.
+ * All calls on one device share that array: calls that overlap in time on
+ * one device (different streams, or different host threads) race and give
+ * wrong results; order them on one stream. `stream` must belong to the
+ * current device (NULL: the current device's default stream).
+ * FA2_ERR_INVALID_ARG, before anything is enqueued, when the plan's
+ * partials (splits * bh * n_q * (head_dim + 1) * 4 bytes, as
+ * fa2_fwd_splitkv_plan reports) exceed the array, or for a stream of another
+ * device; otherwise errors as fa2_fwd_splitkv.
+ */
+int64_t fa2_fwd_splitkv_noalloc_max_bytes(void);
+fa2_status fa2_fwd_splitkv_noalloc(fa2_dtype dt, const void *q, const void *k, const void *v, void *o, float *lse,
+                                   int64_t bh, int64_t n_q, int64_t n_k, int32_t head_dim, float scale,
+                                   int32_t num_splits, void *stream);
+
+/*
  * Backward pre-pass (vision-rs flash_attn2.rs, "Backward - dQ": the per-row
  * term rowsum(O * dO)): delta[b,i] = sum_d o[b,i,d] * d_o[b,i,d] in float32.
  * In: o, d_o [bh,n_q,head_dim] (dt). Out: delta [bh,n_q] float32, fully

@@ -212,3 +212,17 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         _lib.load()
+
+
+def test_splitkv_noalloc_rejects_partials_above_its_scratch():
+    """The allocation-free key-split forward refuses, on the host and before
+    any HIP call, a plan whose float32 partials exceed its static scratch."""
+    lib = fa2.load()
+    cap = lib.fa2_fwd_splitkv_noalloc_max_bytes()
+    assert cap == 32 << 20
+    # 8 ranges x 256 heads x 256 rows x 129 floats = 270 MB
+    assert lib.fa2_fwd_splitkv_noalloc(2, A, A, A, A, A, 256, 256, 4096, 128, 0.088, 8, None) == INVALID
+    assert b"scratch" in lib.fa2_last_error()
+    assert lib.fa2_fwd_splitkv_noalloc(2, A, A, A, A, None, 2, 1, 4096, 128, 0.088, 0, None) == INVALID
+    assert lib.fa2_fwd_splitkv_noalloc(2, A, A, A, A, A, 2, 1, 4096, 48, 0.088, 0, None) == UNSUPPORTED
+    assert lib.fa2_fwd_splitkv_noalloc(2, A, A, A, A, A, 2, 1, 4096, 128, 0.088, -1, None) == INVALID
