@@ -360,6 +360,97 @@ __device__ __forceinline__ typename Traits<DT>::frag ld_vt_frag_tr(const typenam
     return __builtin_bit_cast(typename Traits<DT>::frag, both);
 }
 
+// ---------------------------------------------------------------------------
+// Unpadded 64-row tiles of 16-bit elements filled by buffer -> LDS DMA
+// (gfx950 buffer_load_dwordx4 ... lds: lane i of a wave instruction writes its
+// 16 bytes at LDS base + 16 i, so one instruction fills 1 KiB of consecutive
+// rows). Bank conflicts are avoided by an XOR swizzle of the 16-byte chunks
+// of each row instead of padding: logical chunk c of row r sits at physical
+// chunk c ^ swz(r). The LDS behaves as 64 four-byte banks (256 bytes per bank
+// cycle); ds_read_b128 serves 16 lanes at a time (16 consecutive rows, one
+// chunk each) and ds_read_b64_tr_b16 32 lanes (4 consecutive rows from a
+// multiple of 4, 64 bytes each). swz makes both patterns touch every bank
+// once:
+//   D = 128 (one row per 256 bytes): 4 (r % 4) + (r / 4) % 4
+//   D = 64  (two rows):              4 ((r / 2) % 2) + (r / 4) % 4
+//   D = 32  (four rows):             (r / 4) % 4
+// For the rows a wave reads (32 kb + lane for K; 32 kb + 16 t + 4 hh + l / 4
+// (+ 8) for V) the swizzle does not depend on kb or t, so every fragment
+// address is a per-lane constant plus an immediate offset.
+template <int D>
+__device__ __forceinline__ constexpr int swz(int r) {
+    if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+    else if constexpr (D == 64) return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+    else return (r >> 2) & 3;
+}
+
+template <Dt DT, int D>
+struct SwzTile {
+    static_assert(sizeof(typename Traits<DT>::elem) == 2, "16-bit element types only");
+    using frag = typename Traits<DT>::frag;
+    static constexpr int RB = 2 * D;                    // row bytes
+    static constexpr int NC = RB / 16;                  // 16-byte chunks per row
+    static constexpr int ROWS = 64;
+    static constexpr int BYTES = ROWS * RB;             // one tile
+    static constexpr int PIECES = BYTES / 1024;         // DMA instructions per tile
+    static constexpr int TS = D / 16;                   // contraction steps of a K fragment
+    static constexpr int NDB = D / 32;
+    uint32_t koff[TS];         // K fragment t of row lane % 32 (kb = 0)
+    uint32_t voff[NDB][2];     // V^T read pair (db, lower / upper 8 keys) (kb = t = 0)
+
+    __device__ __forceinline__ void init(int lane) {
+        const int h = lane >> 5, col = lane & 31;
+#pragma unroll
+        for (int t = 0; t < TS; ++t) koff[t] = (uint32_t)(col * RB + (((2 * t + h) ^ swz<D>(col)) << 4));
+        const int l = lane & 15, g = lane >> 4, hh = g >> 1;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int hi = 0; hi < 2; ++hi) {
+                const int r = 4 * hh + (l >> 2) + 8 * hi;
+                const int cb = (32 * db + 16 * (g & 1)) * 2 + 8 * (l & 3);  // logical byte in the row
+                voff[db][hi] = (uint32_t)(r * RB + (((cb >> 4) ^ swz<D>(r)) << 4) + (cb & 15));
+            }
+    }
+    // A/B fragment of K rows 32 kb + lane % 32, contraction step t
+    __device__ __forceinline__ frag k(const char *tile, int kb, int t) const {
+        return *reinterpret_cast<const frag *>(tile + kb * 32 * RB + koff[t]);
+    }
+    // A fragment of V^T (as ld_vt_frag_tr): d block db, keys 32 kb + 16 t ..
+    __device__ __forceinline__ frag vt(const char *tile, int kb, int t, int db) const {
+        typedef short i16x4 __attribute__((ext_vector_type(4)));
+        using lds_i16x4 = __attribute__((address_space(3))) i16x4;
+        const char *base = tile + (32 * kb + 16 * t) * RB;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + voff[db][0]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + voff[db][1]));
+        return __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    // Global byte offset (within a tile) that lane `lane` loads in DMA piece J:
+    // rows J * 1024 / RB .., physical chunk lane % NC, logical chunk
+    // (lane % NC) ^ swz(row).
+    __device__ static __forceinline__ uint32_t piece_off(int J, int lane) {
+        const int row = J * (1024 / RB) + lane / NC, p = lane % NC;
+        return (uint32_t)(row * RB + ((p ^ swz<D>(row)) << 4));
+    }
+};
+
+// One 16-byte-per-lane buffer -> LDS DMA: lane i loads the 16 bytes at
+// byte `voffset` of the buffer `rsrc` and writes them at lds + 16 i (`lds`
+// wave-uniform). Bytes at or past the buffer's end read as zero (hardware
+// range check), so a ragged last tile is zero-filled.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset, char *lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds, 16, voffset, 0, 0,
+                                             0);
+}
+
+// Wait for this wave's outstanding buffer loads (the DMA pieces) only:
+// s_waitcnt vmcnt(0), leaving expcnt and lgkmcnt at their maxima.
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+// After the barrier that publishes DMA-filled LDS: the compiler does not see
+// the DMA as a store to the LDS arrays, so make it assume LDS has changed.
+__device__ __forceinline__ void lds_changed() { __asm__ volatile("" ::: "memory"); }
+
 // Block height that gives each of NT threads one staging block of an R x D
 // tile when possible (4 rows at most).
 template <Dt DT, int R, int D, int NT>

@@ -174,6 +174,208 @@ __device__ __forceinline__ void fwd_tile(const typename Traits<DT>::elem *kt, co
 
 }
 
+// One 64-key tile of the 16-bit forward on DMA-filled swizzled tiles (see
+// SwzTile): the same steps as fwd_tile, with fragment addresses precomputed
+// per lane.
+template <Dt DT, int D, bool MASK, bool FAST, bool FIRST>
+__device__ __forceinline__ void fwd_tile_dma(const char *kt, const char *vt, const SwzTile<DT, D> &sw,
+                                             const typename Traits<DT>::frag (&qf)[D / 16], f32x16 (&acc)[D / 32],
+                                             float &m_ref, float &l_run, float scale_log2, int kvalid, int lane) {
+    using Tr = Traits<DT>;
+    using frag = typename Tr::frag;
+    constexpr int NKB = 2, NDB = D / 32, TS = D / 16, TP = 2;
+    const int h = lane >> 5;
+    f32x16 s[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+        s[kb] = zero16();
+#pragma unroll
+        for (int t = 0; t < TS; ++t) s[kb] = Tr::mfma(sw.k(kt, kb, t), qf[t], s[kb]);
+    }
+    if constexpr (MASK) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int c = 0; c < 16; ++c)
+                if (32 * kb + crow(c, h) >= kvalid) s[kb][c] = -INFINITY;
+    }
+    if constexpr (!FAST || FIRST) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int c = 0; c < 16; ++c) mx = fmaxf(mx, s[kb][c]);
+        const float mx2 = mx * scale_log2;
+        if (__any(mx2 > m_ref + kRescaleLog2)) {
+            __asm__ volatile("" ::: "memory");
+            const float m_new = fmaxf(m_ref, xhalf_max(mx2));
+            const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int c = 0; c < 16; ++c) acc[db][c] *= alpha;
+            l_run *= alpha;
+            m_ref = m_new;
+        }
+    }
+    const float neg_m = -m_ref;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int c = 0; c < 16; ++c) s[kb][c] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][c], scale_log2, neg_m));
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int t = 0; t < TP; ++t) {
+            const frag pf = c_to_frag<DT>(s[kb], t);
+            l_run = Tr::sum_frag(pf, l_run);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) acc[db] = Tr::mfma(sw.vt(vt, kb, t, db), pf, acc[db]);
+        }
+}
+
+// Both passes of the 16-bit forward (see fwd_kernel) on DMA-filled tiles.
+// Tiles go straight from memory into LDS (buffer -> LDS DMA, no register
+// staging) in two stages, each its own LDS array so that the compiler can
+// tell a stage being filled from the stage being read (it then keeps the DMA
+// in flight across the reads instead of waiting for it). Step it issues the
+// DMA of tile it + 1 into the other stage (last read in step it - 1, before
+// that step's barrier), computes tile it, then waits for its own DMA pieces
+// and meets the other waves at the tile's one barrier, which publishes tile
+// it + 1. Past the last tile the DMA reads zeros (buffer range check) into a
+// stage no later step reads.
+template <Dt DT, int D, int WAVES>
+__device__ __forceinline__ void fwd_pass_dma(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                             const typename Traits<DT>::frag (&qf)[D / 16], f32x16 (&acc)[D / 32],
+                                             float &m_ref, float &l_run, float scale_log2, int klen, int lane,
+                                             int wave) {
+    using Sw = SwzTile<DT, D>;
+    constexpr int BC = Sw::ROWS, BYTES = Sw::BYTES, PIECES = Sw::PIECES, NDB = D / 32;
+    __shared__ __attribute__((aligned(1024))) char K0[BYTES];
+    __shared__ __attribute__((aligned(1024))) char K1[BYTES];
+    __shared__ __attribute__((aligned(1024))) char V0[BYTES];
+    __shared__ __attribute__((aligned(1024))) char V1[BYTES];
+    Sw sw;
+    sw.init(lane);
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int ntiles = (klen + BC - 1) / BC;
+    const int nfull = klen / BC;
+    auto dma_tile = [&](int tile, char *kd, char *vd) {
+        const uint32_t t0 = (uint32_t)tile * (uint32_t)BYTES;
+#pragma unroll
+        for (int j = 0; j < (PIECES + WAVES - 1) / WAVES; ++j) {
+            const int J = wv + WAVES * j;
+            if (PIECES % WAVES == 0 || J < PIECES) {
+                const uint32_t off = t0 + Sw::piece_off(J, lane);
+                dma16(krs, off, kd + 1024 * J);
+                dma16(vrs, off, vd + 1024 * J);
+            }
+        }
+    };
+    auto run_pass = [&](auto fast_tag) {
+        constexpr bool FASTP = decltype(fast_tag)::value;
+#pragma unroll
+        for (int i = 0; i < NDB; ++i) acc[i] = zero16();
+        m_ref = -INFINITY;
+        l_run = 0.f;
+        dma_tile(0, K0, V0);
+        wait_dma();
+        __syncthreads();
+        lds_changed();
+        // stage of tile it: K0/V0 for even it, K1/V1 for odd it
+        auto step = [&](auto first_tag, auto odd_tag, int it) {
+            constexpr bool FIRSTP = decltype(first_tag)::value;
+            constexpr bool ODD = decltype(odd_tag)::value;
+            // The scheduling barriers keep the DMA issue ahead of the tile and
+            // the wait for it behind the tile's last products (left to itself
+            // the compiler may sink the issue and hoist the wait, which then
+            // stalls on the DMA right away).
+            dma_tile(it + 1, ODD ? K0 : K1, ODD ? V0 : V1);
+            __builtin_amdgcn_sched_barrier(0);
+            fwd_tile_dma<DT, D, false, FASTP, FIRSTP>(ODD ? K1 : K0, ODD ? V1 : V0, sw, qf, acc, m_ref, l_run,
+                                                       scale_log2, BC, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_dma();
+            __syncthreads();
+            lds_changed();
+        };
+        int it = 0;
+        if (nfull > 0) {
+            step(std::true_type{}, std::false_type{}, 0);
+            it = 1;
+        }
+        for (; it + 1 < nfull; it += 2) {
+            step(std::false_type{}, std::true_type{}, it);
+            step(std::false_type{}, std::false_type{}, it + 1);
+        }
+        if (it < nfull) step(std::false_type{}, std::true_type{}, it++);
+        if (nfull < ntiles) {
+            if (nfull & 1)
+                fwd_tile_dma<DT, D, true, false, true>(K1, V1, sw, qf, acc, m_ref, l_run, scale_log2,
+                                                       klen - nfull * BC, lane);
+            else
+                fwd_tile_dma<DT, D, true, false, true>(K0, V0, sw, qf, acc, m_ref, l_run, scale_log2,
+                                                       klen - nfull * BC, lane);
+        }
+    };
+    run_pass(std::true_type{});
+    // a barrier for the whole workgroup either way: pass 1 refills the stages
+    const bool bad = !(l_run <= 0x1p100f);  // also true for inf and NaN
+    if (__syncthreads_or(bad)) run_pass(std::false_type{});
+}
+
+// The float32 forward: padded tiles staged through registers (K row-major,
+// V transposed so keys are contiguous) in two LDS stages, the exact
+// recurrence (row max on every tile, lazy rescaling) in one pass. After each
+// tile the next tile, already in registers, is stored into the other stage
+// and the one after is fetched; one barrier per tile orders this tile's reads
+// of a stage before that stage is refilled two tiles later.
+template <int D, int WAVES>
+__device__ __forceinline__ void fwd_pass_f32(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                             const float (&qf)[D / 2], f32x16 (&acc)[D / 32], float &m_ref,
+                                             float &l_run, float scale_log2, int klen, int lane, int tid) {
+    constexpr Dt DT = Dt::F32;
+    constexpr int BC = 64, NT = WAVES * 64, NDB = D / 32;
+    constexpr int LDK = D + vec_elems<DT>();
+    constexpr int LDV = fwd_ldv<DT, D, BC>();
+    constexpr int KS = BC * LDK, VS = D * LDV;
+    __shared__ __attribute__((aligned(16))) float Ks[2 * KS];
+    __shared__ __attribute__((aligned(16))) float Vs[2 * VS];
+    RowStage<DT, BC, D, NT> kst;
+    TileStage<DT, BC, D, NT, false, stage_rows<DT, BC, D, NT>()> vst;
+    const int ntiles = (klen + BC - 1) / BC;
+    const int nfull = klen / BC;
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) acc[i] = zero16();
+    m_ref = -INFINITY;
+    l_run = 0.f;
+    kst.load(krs, 0, tid);
+    vst.load(vrs, 0, tid);
+    kst.template store<LDK>(Ks, tid);
+    vst.template store_transposed<LDV>(Vs, tid);
+    if (ntiles > 1) {
+        kst.load(krs, BC, tid);
+        vst.load(vrs, BC, tid);
+    }
+    __syncthreads();
+    for (int it = 0; it < nfull; ++it) {
+        fwd_tile<DT, D, BC, false>(Ks + (it & 1) * KS, Vs + (it & 1) * VS, qf, acc, m_ref, l_run, scale_log2, BC,
+                                   lane);
+        if (it + 1 < ntiles) {
+            kst.template store<LDK>(Ks + ((it + 1) & 1) * KS, tid);
+            vst.template store_transposed<LDV>(Vs + ((it + 1) & 1) * VS, tid);
+            if (it + 2 < ntiles) {
+                kst.load(krs, (it + 2) * BC, tid);
+                vst.load(vrs, (it + 2) * BC, tid);
+            }
+        }
+        __syncthreads();
+    }
+    if (nfull < ntiles)
+        fwd_tile<DT, D, BC, true>(Ks + (nfull & 1) * KS, Vs + (nfull & 1) * VS, qf, acc, m_ref, l_run, scale_log2,
+                                  klen - nfull * BC, lane);
+}
+
 // PARTIAL: key-split mode. The key rows of a head are cut into nsplit
 // consecutive ranges of split_len rows (a multiple of BC; the last range may
 // be shorter); workgroup (bh, split, query block) runs the recurrence over
@@ -188,22 +390,11 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     using Tr = Traits<DT>;
     using elem = typename Tr::elem;
     using frag = typename Tr::frag;
-    constexpr bool TR = sizeof(elem) == 2;  // V read with ds_read_b64_tr_b16
-    constexpr int NT = WAVES * 64;
+    constexpr bool TR = sizeof(elem) == 2;  // 16-bit types: DMA-filled tiles
     constexpr int BR = 32 * WAVES;
-    constexpr int KPL = Tr::KPL;
-    constexpr int KSTEP = 2 * KPL;
-    constexpr int VEC = vec_elems<DT>();
-    constexpr int LDK = D + VEC;            // K tile: row-major, 16-byte pad
-    constexpr int LDV = fwd_ldv<DT, D, BC>();
-    constexpr int KS = BC * LDK;            // elements per K stage
-    constexpr int VS = TR ? BC * LDV : D * LDV;
     constexpr int NDB = D / 32;             // 32-row blocks of O^T
-    constexpr int TS = D / KSTEP;           // contraction steps over head_dim
-    static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
-
-    __shared__ __attribute__((aligned(16))) elem Ks[2 * KS];
-    __shared__ __attribute__((aligned(16))) elem Vs[2 * VS];
+    constexpr int TS = D / (2 * Tr::KPL);   // contraction steps over head_dim
+    static_assert(BC == 64 && D % 32 == 0, "tile shape");
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, col = lane & 31;
@@ -243,97 +434,23 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     float m_ref, l_run;
 
     // K/V tiles: buffer loads over this head's rows (rows past n_k read as
-    // zero) into registers, then into one of two LDS stages.
+    // zero).
     const uint32_t head_bytes = (uint32_t)klen * D * (uint32_t)sizeof(elem);
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + koff, head_bytes);
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + koff, head_bytes);
-    RowStage<DT, BC, D, NT> kst;
-    constexpr int RBS = stage_rows<DT, BC, D, NT>();
-    using VStage = std::conditional_t<TR, RowStage<DT, BC, D, NT>, TileStage<DT, BC, D, NT, false, RBS>>;
-    VStage vst;
-    auto vload = [&](int row0) { vst.load(vrs, row0, tid); };
-    auto vstore = [&](elem *dst) {
-        if constexpr (TR)
-            vst.template store<LDV>(dst, tid);
-        else
-            vst.template store_transposed<LDV>(dst, tid);
-    };
-
-    const int ntiles = (klen + BC - 1) / BC;
-    const int nfull = klen / BC;  // full tiles; a ragged last one follows when klen % BC != 0
-    // Pass 0 takes the row max on the first tile (and on a ragged last one)
-    // only: later probabilities are 2^(s - m_ref) against that reference as
-    // they are. The reference only scales every probability of a row by the
-    // same power of two, which O = acc / l cancels, so this is the same
-    // softmax as long as the values stay in range. If some row of the
-    // workgroup ends with l above 2^100 or not finite (a score about 100 or
-    // more above the first tile's max, in log2 units), the workgroup runs
-    // pass 1: the recurrence with the max taken on every tile (lazy
-    // rescaling).
-    //
-    // After each tile: store the next tile (already in registers) into the
-    // other stage, then fetch the one after. One barrier per tile: it orders this tile's reads of a stage
-    // before that stage is refilled two tiles later.
-    auto advance = [&](int it) {
-        if (it + 1 < ntiles) {
-            kst.template store<LDK>(Ks + ((it + 1) & 1) * KS, tid);
-            vstore(Vs + ((it + 1) & 1) * VS);
-            if (it + 2 < ntiles) {
-                kst.load(krs, (it + 2) * BC, tid);
-                vload((it + 2) * BC);
-            }
-        }
-        __syncthreads();
-    };
-    auto run_pass = [&](auto fast_tag) {
-        constexpr bool FASTP = decltype(fast_tag)::value;
-#pragma unroll
-        for (int i = 0; i < NDB; ++i) acc[i] = zero16();
-        m_ref = -INFINITY;
-        l_run = 0.f;
-        kst.load(krs, 0, tid);
-        vload(0);
-        kst.template store<LDK>(Ks, tid);
-        vstore(Vs);
-        if (ntiles > 1) {
-            kst.load(krs, BC, tid);
-            vload(BC);
-        }
-        __syncthreads();
-        // 16-bit types: the first tile peeled off (FIRST is a template
-        // parameter); float32 keeps one loop over all full tiles (its exact
-        // pass takes the max on every tile either way; the peeled layout
-        // gave wrong outputs for float32 at head_dim 64 with 4 waves, like
-        // the two-pass form below)
-        int it0 = 0;
-        if constexpr (TR) {
-            if (nfull > 0) {
-                fwd_tile<DT, D, BC, false, FASTP, true>(Ks, Vs, qf, acc, m_ref, l_run, scale_log2, BC, lane);
-                advance(0);
-                it0 = 1;
-            }
-        }
-        for (int it = it0; it < nfull; ++it) {
-            fwd_tile<DT, D, BC, false, FASTP, !TR>(Ks + (it & 1) * KS, Vs + (it & 1) * VS, qf, acc, m_ref, l_run,
-                                                   scale_log2, BC, lane);
-            advance(it);
-        }
-        if (nfull < ntiles)
-            fwd_tile<DT, D, BC, true>(Ks + (nfull & 1) * KS, Vs + (nfull & 1) * VS, qf, acc, m_ref, l_run,
-                                      scale_log2, klen - nfull * BC, lane);
-    };
-    if constexpr (TR) {
-        run_pass(std::true_type{});
-        // a barrier for the whole workgroup either way: pass 1 refills the
-        // stages
-        const bool bad = !(l_run <= 0x1p100f);  // also true for inf and NaN
-        if (__syncthreads_or(bad)) run_pass(std::false_type{});
-    } else {
-        // float32 keeps the single exact pass: the two-pass form gave wrong
-        // output channels at head_dim 64 with 4 or 8 waves (a code
-        // generation issue not pinned down; the exact pass is verified)
-        run_pass(std::false_type{});
-    }
+    // Pass 0 (16-bit types) takes the row max on the first tile (and on a
+    // ragged last one) only: later probabilities are 2^(s - m_ref) against
+    // that reference as they are. The reference only scales every
+    // probability of a row by the same power of two, which O = acc / l
+    // cancels, so this is the same softmax as long as the values stay in
+    // range. If some row of the workgroup ends with l above 2^100 or not
+    // finite (a score about 100 or more above the first tile's max, in log2
+    // units), the workgroup runs pass 1: the recurrence with the max taken on
+    // every tile (lazy rescaling). float32 runs that exact recurrence only.
+    if constexpr (TR)
+        fwd_pass_dma<DT, D, WAVES>(krs, vrs, qf, acc, m_ref, l_run, scale_log2, klen, lane, wave);
+    else
+        fwd_pass_f32<D, WAVES>(krs, vrs, qf, acc, m_ref, l_run, scale_log2, klen, lane, tid);
 
     const float l_tot = xhalf_sum(l_run);
     if (qrow < n_q) {
