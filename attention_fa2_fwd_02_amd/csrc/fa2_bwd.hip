@@ -10,6 +10,8 @@
 //                  tiles (the forward's structure with dS in place of P);
 //   dkdv_kernel  - one workgroup per 32*WAVES key rows, looping over query
 //                  tiles; K and V of the wave's 32 keys stay in registers.
+#include <type_traits>
+
 #include "fa2_device.h"
 #include "fa2_launch.h"
 
@@ -150,6 +152,154 @@ struct BwdTile {
     }
 };
 
+// dQ over DMA-filled tiles (16-bit types): K and V tiles of 64 keys go
+// straight from memory into unpadded swizzled LDS tiles (SwzTile), one LDS
+// array per stage, with the forward's step structure (fwd_pass_dma): step it
+// issues the DMA of tile it + 1 into the other stage, computes tile it, waits
+// for its own DMA pieces and meets the other waves at the tile's one barrier.
+// Keys past n_k read as zero rows and add nothing to dQ.
+template <Dt DT, int D, int WAVES>
+__device__ __forceinline__ void dq_pass_dma(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                            const typename Traits<DT>::frag (&qf)[D / 16],
+                                            const typename Traits<DT>::frag (&df)[D / 16], float lse2, float dl,
+                                            f32x16 (&acc)[D / 32], float scale_log2, int n_k, int lane, int wave) {
+    using Tr = Traits<DT>;
+    using frag = typename Tr::frag;
+    using Sw = SwzTile<DT, D>;
+    constexpr int BC = Sw::ROWS, BYTES = Sw::BYTES, PIECES = Sw::PIECES, NDB = D / 32, TS = D / 16;
+    __shared__ __attribute__((aligned(1024))) char K0[BYTES];
+    __shared__ __attribute__((aligned(1024))) char K1[BYTES];
+    __shared__ __attribute__((aligned(1024))) char V0[BYTES];
+    __shared__ __attribute__((aligned(1024))) char V1[BYTES];
+    Sw sw;
+    sw.init(lane);
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int ntiles = (n_k + BC - 1) / BC;
+    auto dma_tile = [&](int tile, char *kd, char *vd) {
+        const uint32_t t0 = (uint32_t)tile * (uint32_t)BYTES;
+#pragma unroll
+        for (int j = 0; j < (PIECES + WAVES - 1) / WAVES; ++j) {
+            const int J = wv + WAVES * j;
+            if (PIECES % WAVES == 0 || J < PIECES) {
+                const uint32_t off = t0 + Sw::piece_off(J, lane);
+                dma16(krs, off, kd + 1024 * J);
+                dma16(vrs, off, vd + 1024 * J);
+            }
+        }
+    };
+    auto tile_fn = [&](const char *kt, const char *vt) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            // the S chain first, so that its exponentials can be scheduled
+            // among the dP products
+            f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+            for (int t = 0; t < TS; ++t) s = Tr::mfma(sw.k(kt, kb, t), qf[t], s);
+#pragma unroll
+            for (int t = 0; t < TS; ++t) dp = Tr::mfma(sw.k(vt, kb, t), df[t], dp);
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c], scale_log2, -lse2));
+                s[c] = p * (dp[c] - dl);
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const frag dsf = c_to_frag<DT>(s, t);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) acc[db] = Tr::mfma(sw.vt(kt, kb, t, db), dsf, acc[db]);
+            }
+        }
+    };
+    dma_tile(0, K0, V0);
+    wait_dma();
+    __syncthreads();
+    lds_changed();
+    // stage of tile it: K0/V0 for even it, K1/V1 for odd it
+    auto step = [&](auto odd_tag, int it) {
+        constexpr bool ODD = decltype(odd_tag)::value;
+        dma_tile(it + 1, ODD ? K0 : K1, ODD ? V0 : V1);
+        __builtin_amdgcn_sched_barrier(0);
+        tile_fn(ODD ? K1 : K0, ODD ? V1 : V0);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_dma();
+        __syncthreads();
+        lds_changed();
+    };
+    int it = 0;
+    for (; it + 1 < ntiles; it += 2) {
+        step(std::false_type{}, it);
+        step(std::true_type{}, it + 1);
+    }
+    if (it < ntiles) step(std::false_type{}, it);
+}
+
+// dQ for float32: padded K and V tiles staged through registers plus a
+// transposed K copy (BwdTile), two LDS stages, one barrier per tile.
+template <int D, int BC, int WAVES>
+__device__ __forceinline__ void dq_pass_f32(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                            const float (&qf)[D / 2], const float (&df)[D / 2], float lse2, float dl,
+                                            f32x16 (&acc)[D / 32], float scale_log2, int n_k, int lane, int tid) {
+    constexpr Dt DT = Dt::F32;
+    using Tr = Traits<DT>;
+    constexpr int NT = WAVES * 64;
+    using Tl = BwdTile<DT, D, false>;
+    constexpr int LDT = BC + 4;          // transposed K copy
+    constexpr int KS = BC * Tl::LD;
+    constexpr int TSZ = D * LDT;
+    constexpr int NKB = BC / 32, NDB = D / 32, TS = D / 2, TP = 16;
+    __shared__ __attribute__((aligned(16))) float Ks[2 * KS];
+    __shared__ __attribute__((aligned(16))) float Vs[2 * KS];
+    __shared__ __attribute__((aligned(16))) float Kt[2 * TSZ];
+    const int h = lane >> 5, col = lane & 31;
+    RowStage<DT, BC, D, NT> kst, vst;
+    TileStage<DT, BC, D, NT, false, stage_rows<DT, BC, D, NT>()> ktst;
+    auto load = [&](int row0) {
+        kst.load(krs, row0, tid);
+        vst.load(vrs, row0, tid);
+        ktst.load(krs, row0, tid);
+    };
+    auto store = [&](int stage) {
+        Tl::store(kst, Ks + stage * KS, tid);
+        Tl::store(vst, Vs + stage * KS, tid);
+        ktst.template store_transposed<LDT>(Kt + stage * TSZ, tid);
+    };
+    const int ntiles = (n_k + BC - 1) / BC;
+    load(0);
+    store(0);
+    if (ntiles > 1) load(BC);
+    __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+        const int st = it & 1;
+        const float *kt = Ks + st * KS, *vt = Vs + st * KS, *ktt = Kt + st * TSZ;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+            for (int t = 0; t < TS; ++t) {
+                s = Tr::mfma(Tl::row(kt, 32 * kb + col, t, h), qf[t], s);
+                dp = Tr::mfma(Tl::row(vt, 32 * kb + col, t, h), df[t], dp);
+            }
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c], scale_log2, -lse2));
+                s[c] = p * (dp[c] - dl);
+            }
+#pragma unroll
+            for (int t = 0; t < TP; ++t) {
+                const float dsf = c_to_frag<DT>(s, t);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    acc[db] = Tr::mfma(Tl::template trans<LDT>(kt, ktt, kb, t, db, lane), dsf, acc[db]);
+            }
+        }
+        if (it + 1 < ntiles) {
+            store((it + 1) & 1);
+            if (it + 2 < ntiles) load((it + 2) * BC);
+        }
+        __syncthreads();
+    }
+}
+
 // ---------------------------------------------------------------------------
 // dQ: per workgroup BR = 32*WAVES query rows (one 32-row block per wave, each
 // lane owning one query column), looping over key tiles of BC rows:
@@ -166,22 +316,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     using elem = typename Tr::elem;
     using frag = typename Tr::frag;
     constexpr bool TR = sizeof(elem) == 2;
-    constexpr int NT = WAVES * 64;
     constexpr int BR = 32 * WAVES;
-    constexpr int KPL = Tr::KPL;
-    constexpr int KSTEP = 2 * KPL;
-    using Tl = BwdTile<DT, D, false>;
-    constexpr int LDT = BC + 4;          // float32 transposed K copy
-    constexpr int KS = BC * Tl::LD;
-    constexpr int TSZ = TR ? 1 : D * LDT;
-    constexpr int NKB = BC / 32;
     constexpr int NDB = D / 32;
-    constexpr int TS = D / KSTEP;
-    constexpr int TP = 32 / KSTEP;
-
-    __shared__ __attribute__((aligned(16))) elem Ks[2 * KS];
-    __shared__ __attribute__((aligned(16))) elem Vs[2 * KS];
-    __shared__ __attribute__((aligned(16))) elem Kt[2 * TSZ];
+    constexpr int TS = D / (2 * Tr::KPL);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, col = lane & 31;
@@ -217,67 +354,11 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     const uint32_t head_bytes = (uint32_t)n_k * D * (uint32_t)sizeof(elem);
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + koff, head_bytes);
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + koff, head_bytes);
-    RowStage<DT, BC, D, NT> kst, vst;
-    constexpr int RBS = stage_rows<DT, BC, D, NT>();
-    TileStage<DT, BC, D, NT, false, RBS> ktst;  // float32 only: transposed K
-    auto load = [&](int row0) {
-        kst.load(krs, row0, tid);
-        vst.load(vrs, row0, tid);
-        if constexpr (!TR) ktst.load(krs, row0, tid);
-    };
-    auto store = [&](int stage) {
-        Tl::store(kst, Ks + stage * KS, tid);
-        Tl::store(vst, Vs + stage * KS, tid);
-        if constexpr (!TR) ktst.template store_transposed<LDT>(Kt + stage * TSZ, tid);
-    };
-
-    const int ntiles = (n_k + BC - 1) / BC;
-    load(0);
-    store(0);
-    if (ntiles > 1) load(BC);
-    __syncthreads();
-
-    for (int it = 0; it < ntiles; ++it) {
-        const int st = it & 1;
-        const elem *kt = Ks + st * KS;
-        const elem *vt = Vs + st * KS;
-        const elem *ktt = Kt + st * TSZ;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            f32x16 s = zero16(), dp = zero16();
-            if constexpr (TR) {
-                // 16-bit types: the S chain first, so that its exponentials
-                // can be scheduled among the dP products (1% faster at the
-                // LLM shape, same results)
-#pragma unroll
-                for (int t = 0; t < TS; ++t) s = Tr::mfma(Tl::row(kt, 32 * kb + col, t, h), qf[t], s);
-#pragma unroll
-                for (int t = 0; t < TS; ++t) dp = Tr::mfma(Tl::row(vt, 32 * kb + col, t, h), df[t], dp);
-            } else {
-#pragma unroll
-                for (int t = 0; t < TS; ++t) {
-                    s = Tr::mfma(Tl::row(kt, 32 * kb + col, t, h), qf[t], s);
-                    dp = Tr::mfma(Tl::row(vt, 32 * kb + col, t, h), df[t], dp);
-                }
-            }
-#pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c], scale_log2, -lse2));
-                s[c] = p * (dp[c] - dl);
-            }
-#pragma unroll
-            for (int t = 0; t < TP; ++t) {
-                const frag dsf = c_to_frag<DT>(s, t);
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    acc[db] = Tr::mfma(Tl::template trans<LDT>(kt, ktt, kb, t, db, lane), dsf, acc[db]);
-            }
-        }
-        if (it + 1 < ntiles) {
-            store((it + 1) & 1);
-            if (it + 2 < ntiles) load((it + 2) * BC);
-        }
-        __syncthreads();
+    if constexpr (TR) {
+        static_assert(BC == 64, "DMA tiles hold 64 keys");
+        dq_pass_dma<DT, D, WAVES>(krs, vrs, qf, df, lse2, dl, acc, scale_log2, n_k, lane, wave);
+    } else {
+        dq_pass_f32<D, BC, WAVES>(krs, vrs, qf, df, lse2, dl, acc, scale_log2, n_k, lane, tid);
     }
 
     if (qvalid) {
@@ -290,112 +371,214 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: per workgroup BKV = 32*WAVES key rows, wave w owning keys
-// 32w..32w+31 as B operands: K rows in registers, V rows in LDS for 16-bit
-// types (read once per 32-query block; that keeps a wave within 256 VGPRs,
-// i.e. two waves per SIMD) and in registers for float32. Query tiles
-// of BQ rows: Q and dO row-major in LDS (A operands of S = Q K^T and
-// dP = dO V^T, and via transposing reads of dK^T += Q^T dS and
-// dV^T += dO^T P), plus lse*log2e and delta. C blocks: rows = queries,
-// column = key; lse and delta vary along a lane's registers.
-template <Dt DT, int D, int BQ, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_kernel(
-    const typename Traits<DT>::elem *__restrict__ Q, const typename Traits<DT>::elem *__restrict__ K,
-    const typename Traits<DT>::elem *__restrict__ V, const typename Traits<DT>::elem *__restrict__ dO,
-    const float *__restrict__ LSE, const float *__restrict__ Delta, typename Traits<DT>::elem *__restrict__ dK,
-    typename Traits<DT>::elem *__restrict__ dV, int n_q, int n_k, int n_kblocks, int total_blocks,
-    float scale_log2, float scale) {
+// dK, dV over DMA-filled tiles (16-bit types). Each wave's own 32 V rows go
+// once into a wave-private swizzled LDS tile (B operand of dP = dO V^T, read
+// again for every query tile; in registers they would take the wave past 256
+// VGPRs); query tiles of 32 rows of Q and dO go by DMA into swizzled tiles,
+// one LDS array per stage, with the forward's step structure (fwd_pass_dma).
+// lse (times log2 e) and delta of a tile come through registers of the first
+// 32 lanes, one tile ahead. Queries past n_q read as zero Q and dO rows and
+// add nothing. At the end each wave stages its dK and dV rows through its
+// own V tile and writes whole 16-byte pieces of full rows.
+template <Dt DT, int D, int WAVES>
+__device__ __forceinline__ void dkdv_pass_dma(__amdgpu_buffer_rsrc_t qrs, __amdgpu_buffer_rsrc_t drs,
+                                              __amdgpu_buffer_rsrc_t vrs, __amdgpu_buffer_rsrc_t lrs,
+                                              __amdgpu_buffer_rsrc_t ers,
+                                              const typename Traits<DT>::frag (&kf)[D / 16],
+                                              typename Traits<DT>::elem *__restrict__ dk_rows,
+                                              typename Traits<DT>::elem *__restrict__ dv_rows, int krow0, int n_k,
+                                              int n_q, float scale_log2, float scale, int lane, int wave, int tid) {
     using Tr = Traits<DT>;
     using elem = typename Tr::elem;
     using frag = typename Tr::frag;
-    constexpr bool TR = sizeof(elem) == 2;
-    constexpr int NT = WAVES * 64;
-    constexpr int BKV = 32 * WAVES;
-    constexpr int KPL = Tr::KPL;
-    constexpr int KSTEP = 2 * KPL;
-    using Tl = BwdTile<DT, D, true>;
-    constexpr int LDT = BQ + 4;          // float32 transposed copies
-    constexpr int QS = BQ * Tl::LD;
-    constexpr int TSZ = TR ? 1 : D * LDT;
-    constexpr int NQB = BQ / 32;
-    constexpr int NDB = D / 32;
-    constexpr int TS = D / KSTEP;
-    constexpr int TP = 32 / KSTEP;
-    static_assert(BQ <= NT, "lse staging");
+    using Sw = SwzTile<DT, D, 32>;
+    constexpr int BQ = Sw::ROWS, BYTES = Sw::BYTES, PIECES = Sw::PIECES, NDB = D / 32, TS = D / 16;
+    constexpr int RB = Sw::RB, NC = Sw::NC;
+    __shared__ __attribute__((aligned(1024))) char Q0[BYTES];
+    __shared__ __attribute__((aligned(1024))) char Q1[BYTES];
+    __shared__ __attribute__((aligned(1024))) char D0[BYTES];
+    __shared__ __attribute__((aligned(1024))) char D1[BYTES];
+    // 16-byte aligned (the DMA needs no more), so that the LDS layout puts
+    // the 1024-aligned per-tile arrays first, within reach of the 16-bit
+    // immediate offsets of the LDS reads
+    __shared__ __attribute__((aligned(16))) char Vw[WAVES * BYTES];
+    __shared__ __attribute__((aligned(16))) float L0[BQ];
+    __shared__ __attribute__((aligned(16))) float L1[BQ];
+    __shared__ __attribute__((aligned(16))) float E0[BQ];
+    __shared__ __attribute__((aligned(16))) float E1[BQ];
+    const int h = lane >> 5;
+    Sw sw;
+    sw.init(lane);
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    char *vown = Vw + wv * BYTES;
+    const int ntiles = (n_q + BQ - 1) / BQ;
 
-    __shared__ __attribute__((aligned(16))) elem Qs[2 * QS];
-    __shared__ __attribute__((aligned(16))) elem Ds[2 * QS];
-    __shared__ __attribute__((aligned(16))) elem Qt[2 * TSZ];
-    __shared__ __attribute__((aligned(16))) elem Dt_[2 * TSZ];
-    __shared__ __attribute__((aligned(16))) float Ls[2 * BQ];
-    __shared__ __attribute__((aligned(16))) float Dl[2 * BQ];
-    constexpr bool VLDS = TR;
-    __shared__ __attribute__((aligned(16))) elem Vk[VLDS ? BKV * Tl::LD : 1];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int h = lane >> 5, col = lane & 31;
-    const int blk = xcd_remap(blockIdx.x, total_blocks);
-    const int bh = blk / n_kblocks, kblk = blk % n_kblocks;
-    const int krow = kblk * BKV + wave * 32 + col;
-    const int64_t qoff = (int64_t)bh * n_q * D;
-    const int64_t koff = (int64_t)bh * n_k * D;
-    const int64_t loff = (int64_t)bh * n_q;
-
-    frag kf[TS], vf[VLDS ? 1 : TS];
-    if (krow < n_k) {
-        const elem *kp = K + koff + (int64_t)krow * D;
+    auto dma_tile = [&](int tile, char *qd, char *dd) {
+        const uint32_t t0 = (uint32_t)tile * (uint32_t)BYTES;
 #pragma unroll
-        for (int t = 0; t < TS; ++t) kf[t] = ld_row_frag<DT>(kp, t, h);
-        if constexpr (!VLDS) {
-            const elem *vp = V + koff + (int64_t)krow * D;
-#pragma unroll
-            for (int t = 0; t < TS; ++t) vf[t] = ld_row_frag<DT>(vp, t, h);
+        for (int j = 0; j < (PIECES + WAVES - 1) / WAVES; ++j) {
+            const int J = wv + WAVES * j;
+            if (PIECES % WAVES == 0 || J < PIECES) {
+                const uint32_t off = t0 + Sw::piece_off(J, lane);
+                dma16(qrs, off, qd + 1024 * J);
+                dma16(drs, off, dd + 1024 * J);
+            }
         }
-    } else {
-#pragma unroll
-        for (int t = 0; t < TS; ++t) kf[t] = zero_frag_b<DT>();
-        if constexpr (!VLDS) {
-#pragma unroll
-            for (int t = 0; t < TS; ++t) vf[t] = zero_frag_b<DT>();
+    };
+    // lse * log2e and delta of query tile `tile` (rows past n_q read as 0: their
+    // Q and dO rows are zero, so their terms vanish whatever P is)
+    float lreg = 0.f, dreg = 0.f;
+    auto load_ld = [&](int tile) {
+        if (tid < BQ) {
+            lreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrs, (tile * BQ + tid) * 4, 0, 0));
+            dreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ers, (tile * BQ + tid) * 4, 0, 0));
         }
-    }
-    if constexpr (VLDS) {
-        // this workgroup's V rows (rows past n_k read as zero)
-        const __amdgpu_buffer_rsrc_t vrs =
-            make_rsrc(V + koff, (uint32_t)n_k * D * (uint32_t)sizeof(elem));
-        RowStage<DT, BKV, D, NT> vst;
-        vst.load(vrs, kblk * BKV, tid);
-        Tl::store(vst, Vk, tid);
-        // made visible by the barrier after the first query tile is staged
-    }
-    const elem *vkrow = Tl::row_ptr(Vk, wave * 32 + col);
+    };
+    auto store_ld = [&](float *ld, float *ed) {
+        if (tid < BQ) {
+            ld[tid] = lreg * kLog2e;
+            ed[tid] = dreg;
+        }
+    };
 
     f32x16 accK[NDB], accV[NDB];
 #pragma unroll
     for (int i = 0; i < NDB; ++i) accK[i] = accV[i] = zero16();
 
-    const uint32_t head_bytes = (uint32_t)n_q * D * (uint32_t)sizeof(elem);
-    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + qoff, head_bytes);
-    const __amdgpu_buffer_rsrc_t drs = make_rsrc(dO + qoff, head_bytes);
-    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(LSE + loff, (uint32_t)n_q * 4u);
-    const __amdgpu_buffer_rsrc_t ers = make_rsrc(Delta + loff, (uint32_t)n_q * 4u);
+    auto tile_fn = [&](const char *qt, const char *dt, const float *ls, const float *es) {
+        f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+        for (int t = 0; t < TS; ++t) {
+            s = Tr::mfma(sw.k(qt, 0, t), kf[t], s);
+            dp = Tr::mfma(sw.k(dt, 0, t), sw.k(vown, 0, t), dp);
+        }
+        // p into s, dS into dp (rows = queries along a lane's registers)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float4 l4 = *reinterpret_cast<const float4 *>(ls + 8 * g + 4 * h);
+            const float4 d4 = *reinterpret_cast<const float4 *>(es + 8 * g + 4 * h);
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+            const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = 4 * g + i;
+                const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c], scale_log2, -lv[i]));
+                s[c] = pv;
+                dp[c] = pv * (dp[c] - dv[i]);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const frag pf = c_to_frag<DT>(s, t);
+            const frag dsf = c_to_frag<DT>(dp, t);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                accV[db] = Tr::mfma(sw.vt(dt, 0, t, db), pf, accV[db]);
+                accK[db] = Tr::mfma(sw.vt(qt, 0, t, db), dsf, accK[db]);
+            }
+        }
+    };
+
+    // prologue: the wave's V rows, query tile 0 and its lse / delta; tile 1's
+    // lse / delta into registers
+#pragma unroll
+    for (int J = 0; J < PIECES; ++J) dma16(vrs, (uint32_t)(krow0 + 32 * wv) * RB + Sw::piece_off(J, lane), vown + 1024 * J);
+    dma_tile(0, Q0, D0);
+    load_ld(0);
+    wait_dma();
+    store_ld(L0, E0);
+    load_ld(1);
+    wait_dma();
+    __syncthreads();
+    lds_changed();
+    // stage of tile it: Q0/D0/L0/E0 for even it, the others for odd it
+    auto step = [&](auto odd_tag, int it) {
+        constexpr bool ODD = decltype(odd_tag)::value;
+        dma_tile(it + 1, ODD ? Q0 : Q1, ODD ? D0 : D1);
+        store_ld(ODD ? L0 : L1, ODD ? E0 : E1);
+        load_ld(it + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        tile_fn(ODD ? Q1 : Q0, ODD ? D1 : D0, ODD ? L1 : L0, ODD ? E1 : E0);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_dma();
+        __syncthreads();
+        lds_changed();
+    };
+    int it = 0;
+    for (; it + 1 < ntiles; it += 2) {
+        step(std::false_type{}, it);
+        step(std::true_type{}, it + 1);
+    }
+    if (it < ntiles) step(std::false_type{}, it);
+
+    // Epilogue through the wave's own V tile (no other wave reads it): lane
+    // `col` holds dK / dV of key col, d = 32 db + 8 g + 4 h + 0..3; it writes
+    // those 8 bytes at the swizzled place of row col, then the wave reads
+    // back whole 16-byte chunks, 16 lanes per 256-byte row, and stores them.
+    const int col = lane & 31;
+    auto emit = [&](const f32x16 (&acc)[NDB], float mul, elem *rows) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                typename Tr::half_frag v;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = static_cast<elem>(acc[db][4 * g + i] * mul);
+                const int c = 4 * db + g;  // logical chunk of d = 32 db + 8 g
+                *reinterpret_cast<typename Tr::half_frag *>(vown + col * RB + ((c ^ swz<D>(col)) << 4) + 8 * h) = v;
+            }
+        constexpr int PER = 32 * NC / 64;  // chunks per lane
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = lane + 64 * i, r = idx / NC, p = idx % NC;
+            const uint4 w = *reinterpret_cast<const uint4 *>(vown + r * RB + (p << 4));
+            const int c = p ^ swz<D>(r);
+            if (krow0 + 32 * wv + r < n_k)
+                *reinterpret_cast<uint4 *>(rows + (int64_t)(32 * wv + r) * D + c * 8) = w;
+        }
+    };
+    emit(accK, scale, dk_rows);
+    emit(accV, 1.f, dv_rows);
+}
+
+// dK, dV for float32: K and V rows of the wave's keys in registers; query
+// tiles of BQ rows of Q and dO staged through registers into padded tiles plus
+// transposed copies, with lse * log2e and delta, two LDS stages.
+template <int D, int BQ, int WAVES>
+__device__ __forceinline__ void dkdv_pass_f32(__amdgpu_buffer_rsrc_t qrs, __amdgpu_buffer_rsrc_t drs,
+                                              __amdgpu_buffer_rsrc_t lrs, __amdgpu_buffer_rsrc_t ers,
+                                              const float (&kf)[D / 2], const float (&vf)[D / 2],
+                                              f32x16 (&accK)[D / 32], f32x16 (&accV)[D / 32], int n_q,
+                                              float scale_log2, int lane, int tid) {
+    constexpr Dt DT = Dt::F32;
+    using Tr = Traits<DT>;
+    constexpr int NT = WAVES * 64;
+    using Tl = BwdTile<DT, D, true>;
+    constexpr int LDT = BQ + 4;
+    constexpr int QS = BQ * Tl::LD;
+    constexpr int TSZ = D * LDT;
+    constexpr int NQB = BQ / 32, NDB = D / 32, TS = D / 2, TP = 16;
+    static_assert(BQ <= NT, "lse staging");
+    __shared__ __attribute__((aligned(16))) float Qs[2 * QS];
+    __shared__ __attribute__((aligned(16))) float Ds[2 * QS];
+    __shared__ __attribute__((aligned(16))) float Qt[2 * TSZ];
+    __shared__ __attribute__((aligned(16))) float Dt_[2 * TSZ];
+    __shared__ __attribute__((aligned(16))) float Ls[2 * BQ];
+    __shared__ __attribute__((aligned(16))) float Dl[2 * BQ];
+    const int h = lane >> 5, col = lane & 31;
     RowStage<DT, BQ, D, NT> qst, dst;
     constexpr int RBS = stage_rows<DT, BQ, D, NT>();
-    TileStage<DT, BQ, D, NT, false, RBS> qtst, dtst;  // float32 only: transposed copies
+    TileStage<DT, BQ, D, NT, false, RBS> qtst, dtst;
     float lreg = 0.f, dreg = 0.f;
     auto load = [&](int row0) {
         qst.load(qrs, row0, tid);
         dst.load(drs, row0, tid);
         if (tid < BQ) {
-            // rows past n_q read as 0: their Q and dO rows are zero, so their
-            // terms vanish whatever P is
             lreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrs, (row0 + tid) * 4, 0, 0));
             dreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ers, (row0 + tid) * 4, 0, 0));
         }
-        if constexpr (!TR) {
-            qtst.load(qrs, row0, tid);
-            dtst.load(drs, row0, tid);
-        }
+        qtst.load(qrs, row0, tid);
+        dtst.load(drs, row0, tid);
     };
     auto store = [&](int stage) {
         Tl::store(qst, Qs + stage * QS, tid);
@@ -404,38 +587,26 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
             Ls[stage * BQ + tid] = lreg * kLog2e;
             Dl[stage * BQ + tid] = dreg;
         }
-        if constexpr (!TR) {
-            qtst.template store_transposed<LDT>(Qt + stage * TSZ, tid);
-            dtst.template store_transposed<LDT>(Dt_ + stage * TSZ, tid);
-        }
+        qtst.template store_transposed<LDT>(Qt + stage * TSZ, tid);
+        dtst.template store_transposed<LDT>(Dt_ + stage * TSZ, tid);
     };
-
     const int ntiles = (n_q + BQ - 1) / BQ;
     load(0);
     store(0);
     if (ntiles > 1) load(BQ);
     __syncthreads();
-
     for (int it = 0; it < ntiles; ++it) {
         const int st = it & 1;
-        const elem *qt = Qs + st * QS;
-        const elem *dt = Ds + st * QS;
-        const elem *qtt = Qt + st * TSZ;
-        const elem *dtt = Dt_ + st * TSZ;
-        const float *ls = Ls + st * BQ;
-        const float *dls = Dl + st * BQ;
+        const float *qt = Qs + st * QS, *dt = Ds + st * QS, *qtt = Qt + st * TSZ, *dtt = Dt_ + st * TSZ;
+        const float *ls = Ls + st * BQ, *dls = Dl + st * BQ;
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
             f32x16 s = zero16(), dp = zero16();
 #pragma unroll
             for (int t = 0; t < TS; ++t) {
                 s = Tr::mfma(Tl::row(qt, 32 * qb + col, t, h), kf[t], s);
-                if constexpr (VLDS)
-                    dp = Tr::mfma(Tl::row(dt, 32 * qb + col, t, h), ld_row_frag<DT>(vkrow, t, h), dp);
-                else
-                    dp = Tr::mfma(Tl::row(dt, 32 * qb + col, t, h), vf[t], dp);
+                dp = Tr::mfma(Tl::row(dt, 32 * qb + col, t, h), vf[t], dp);
             }
-            // p into s, dS into dp
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const float4 l4 = *reinterpret_cast<const float4 *>(ls + 32 * qb + 8 * g + 4 * h);
@@ -452,8 +623,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
             }
 #pragma unroll
             for (int t = 0; t < TP; ++t) {
-                const frag pf = c_to_frag<DT>(s, t);
-                const frag dsf = c_to_frag<DT>(dp, t);
+                const float pf = c_to_frag<DT>(s, t);
+                const float dsf = c_to_frag<DT>(dp, t);
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
                     accV[db] = Tr::mfma(Tl::template trans<LDT>(dt, dtt, qb, t, db, lane), pf, accV[db]);
@@ -467,17 +638,87 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
         }
         __syncthreads();
     }
+}
 
+// dK, dV: per workgroup BKV = 32*WAVES key rows, wave w owning keys
+// 32w..32w+31 as B operands (K rows in registers). Query tiles of BQ rows:
+// Q and dO as A operands of S = Q K^T and dP = dO V^T, and via transposing
+// reads of dK^T += Q^T dS and dV^T += dO^T P, plus lse*log2e and delta.
+// C blocks: rows = queries, column = key; lse and delta vary along a lane's
+// registers.
+template <Dt DT, int D, int BQ, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_kernel(
+    const typename Traits<DT>::elem *__restrict__ Q, const typename Traits<DT>::elem *__restrict__ K,
+    const typename Traits<DT>::elem *__restrict__ V, const typename Traits<DT>::elem *__restrict__ dO,
+    const float *__restrict__ LSE, const float *__restrict__ Delta, typename Traits<DT>::elem *__restrict__ dK,
+    typename Traits<DT>::elem *__restrict__ dV, int n_q, int n_k, int n_kblocks, int total_blocks,
+    float scale_log2, float scale) {
+    using Tr = Traits<DT>;
+    using elem = typename Tr::elem;
+    using frag = typename Tr::frag;
+    constexpr bool TR = sizeof(elem) == 2;
+    constexpr int BKV = 32 * WAVES;
+    constexpr int NDB = D / 32;
+    constexpr int TS = D / (2 * Tr::KPL);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int h = lane >> 5, col = lane & 31;
+    const int blk = xcd_remap(blockIdx.x, total_blocks);
+    const int bh = blk / n_kblocks, kblk = blk % n_kblocks;
+    const int krow = kblk * BKV + wave * 32 + col;
+    const int64_t qoff = (int64_t)bh * n_q * D;
+    const int64_t koff = (int64_t)bh * n_k * D;
+    const int64_t loff = (int64_t)bh * n_q;
+
+    frag kf[TS];
     if (krow < n_k) {
-        elem *kp = dK + koff + (int64_t)krow * D;
-        elem *vp = dV + koff + (int64_t)krow * D;
+        const elem *kp = K + koff + (int64_t)krow * D;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+        for (int t = 0; t < TS; ++t) kf[t] = ld_row_frag<DT>(kp, t, h);
+    } else {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                store4_b<DT>(kp + 32 * db + 8 * g + 4 * h, accK[db], g, scale);
-                store4_b<DT>(vp + 32 * db + 8 * g + 4 * h, accV[db], g, 1.f);
-            }
+        for (int t = 0; t < TS; ++t) kf[t] = zero_frag_b<DT>();
+    }
+
+    const uint32_t head_bytes = (uint32_t)n_q * D * (uint32_t)sizeof(elem);
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + qoff, head_bytes);
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(dO + qoff, head_bytes);
+    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(LSE + loff, (uint32_t)n_q * 4u);
+    const __amdgpu_buffer_rsrc_t ers = make_rsrc(Delta + loff, (uint32_t)n_q * 4u);
+
+    if constexpr (TR) {
+        static_assert(BQ == 32, "DMA query tiles hold 32 rows");
+        // V rows past n_k read as zero
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + koff, (uint32_t)n_k * D * (uint32_t)sizeof(elem));
+        const int krow0 = kblk * BKV;
+        dkdv_pass_dma<DT, D, WAVES>(qrs, drs, vrs, lrs, ers, kf, dK + koff + (int64_t)krow0 * D,
+                                    dV + koff + (int64_t)krow0 * D, krow0, n_k, n_q, scale_log2, scale, lane, wave,
+                                    tid);
+    } else {
+        frag vf[TS];
+        if (krow < n_k) {
+            const elem *vp = V + koff + (int64_t)krow * D;
+#pragma unroll
+            for (int t = 0; t < TS; ++t) vf[t] = ld_row_frag<DT>(vp, t, h);
+        } else {
+#pragma unroll
+            for (int t = 0; t < TS; ++t) vf[t] = zero_frag_b<DT>();
+        }
+        f32x16 accK[NDB], accV[NDB];
+#pragma unroll
+        for (int i = 0; i < NDB; ++i) accK[i] = accV[i] = zero16();
+        dkdv_pass_f32<D, BQ, WAVES>(qrs, drs, lrs, ers, kf, vf, accK, accV, n_q, scale_log2, lane, tid);
+        if (krow < n_k) {
+            elem *kp = dK + koff + (int64_t)krow * D;
+            elem *vp = dV + koff + (int64_t)krow * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    store4_b<DT>(kp + 32 * db + 8 * g + 4 * h, accK[db], g, scale);
+                    store4_b<DT>(vp + 32 * db + 8 * g + 4 * h, accV[db], g, 1.f);
+                }
+        }
     }
 }
 

@@ -361,7 +361,7 @@ __device__ __forceinline__ typename Traits<DT>::frag ld_vt_frag_tr(const typenam
 }
 
 // ---------------------------------------------------------------------------
-// Unpadded 64-row tiles of 16-bit elements filled by buffer -> LDS DMA
+// Unpadded tiles (64 or 32 rows) of 16-bit elements filled by buffer -> LDS DMA
 // (gfx950 buffer_load_dwordx4 ... lds: lane i of a wave instruction writes its
 // 16 bytes at LDS base + 16 i, so one instruction fills 1 KiB of consecutive
 // rows). Bank conflicts are avoided by an XOR swizzle of the 16-byte chunks
@@ -384,13 +384,13 @@ __device__ __forceinline__ constexpr int swz(int r) {
     else return (r >> 2) & 3;
 }
 
-template <Dt DT, int D>
+template <Dt DT, int D, int ROWS_ = 64>
 struct SwzTile {
     static_assert(sizeof(typename Traits<DT>::elem) == 2, "16-bit element types only");
     using frag = typename Traits<DT>::frag;
     static constexpr int RB = 2 * D;                    // row bytes
     static constexpr int NC = RB / 16;                  // 16-byte chunks per row
-    static constexpr int ROWS = 64;
+    static constexpr int ROWS = ROWS_;                  // a multiple of 32
     static constexpr int BYTES = ROWS * RB;             // one tile
     static constexpr int PIECES = BYTES / 1024;         // DMA instructions per tile
     static constexpr int TS = D / 16;                   // contraction steps of a K fragment
