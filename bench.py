@@ -8,8 +8,9 @@ algorithmic throughput by the FLOP convention fwd = 4 BH Nq Nk D, bwd = 2.5 x
 fwd. Per-kernel durations come from HIP events recorded around every launch
 on the launch stream inside the timed region.
 
-Legs measured in the same run (not part of `value`): the forward alone at
-that shape, cross-attention (BH 1024, Nq 1024, Nk 8192, D 64, K x 3), the
+Legs measured in the same run (not part of `value`): the tiny float32
+forward (BH 2, N 64, D 32), the forward alone at the LLM shape,
+cross-attention (BH 1024, Nq 1024, Nk 8192, D 64, K x 3), the
 backward-config step (BH 256, N 2048, D 128), the C2PSA block (pack,
 attention twice, merge, and the fused kernel) warm and with L2/MALL flushed
 before each call, and its backward (composed and fused), a decoding shape
@@ -17,8 +18,16 @@ before each call, and its backward (composed and fused), a decoding shape
 the plain forward, and a reference bf16 GEMM (random and constant operands)
 that shows the chip's practical dense-MFMA ceiling on random data.
 
+Per-kernel work is reported two ways: executed MFMA work (the products a
+kernel runs: forward S and P V, 4 units of BH Nq Nk D; dkdv S, dP, dV, dK, 8
+units; dq S, dP, dQ, 6 units) and algorithmic work (what the FLOP convention
+counts once: forward 4 units, dkdv 8, dq 2 -- its S and dP products repeat
+dkdv's and are the price of the atomic-free split).
+
 The CPU baseline times the fp64 oracle on a bounded sample of the same
-workload (a few heads at full sequence length) on the host cores.
+workload (a few heads at full sequence length) on the host cores, and each
+configuration's oracle (C1 and C2 on their full inputs, C3, C4 and C5 on a
+few full-length heads) beside the GPU time of the same configuration.
 
 Prints one JSON line.
 """
@@ -50,7 +59,7 @@ def _parse():
     ap.add_argument("--no-legs", action="store_true", help="skip the other-shape legs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0, help="oracle sample heads (0: three per thread)")
-    ap.add_argument("--only", choices=["main", "c3_fwd", "c4", "c5", "c2", "decode", "gemm_ref", "vendor_ref"], default=None,
+    ap.add_argument("--only", choices=["main", "c1", "c3_fwd", "c4", "c5", "c2", "decode", "gemm_ref"], default=None,
                     help="run just the main step or just one leg (for profiling one workload); prints no JSON "
                          "line unless it is the main step")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -169,26 +178,31 @@ def main():
     step_fl = fwd_fl + w3.bwd_flops()
     value = step_fl / (ms_step * 1e-3) / 1e12
 
-    # per-kernel algorithmic work per launch
+    # per-kernel work per launch, in units of BH Nq Nk D flops: executed MFMA
+    # work and the algorithmic share (the backward's 10 units counted once:
+    # dkdv's S, dP, dV, dK products are all required, dq adds only dQ)
     nqnkd = w3.bh * w3.n_q * w3.n_k * w3.head_dim
-    kern_flops = {"fwd": 4.0 * nqnkd, "dkdv": 8.0 * nqnkd, "dq": 6.0 * nqnkd}
+    exec_units = {"fwd": 4.0, "dkdv": 8.0, "dq": 6.0}
+    algo_units = {"fwd": 4.0, "dkdv": 8.0, "dq": 2.0}
     es = 2
     kern_bytes = {"delta": 2 * w3.bh * w3.n_q * w3.head_dim * es + w3.bh * w3.n_q * 4}
     kernels = {}
     for name in ("fwd", "delta", "dkdv", "dq"):
         ms = timer.avg_ms(name)
         ent = {"avg_ms": round(ms, 4)}
-        if name in kern_flops:
-            tf = kern_flops[name] / (ms * 1e-3) / 1e12
-            ent.update({"tflops": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+        if name in exec_units:
+            tf_a = algo_units[name] * nqnkd / (ms * 1e-3) / 1e12
+            tf_x = exec_units[name] * nqnkd / (ms * 1e-3) / 1e12
+            ent.update({"tflops_algorithmic": round(tf_a, 1), "frac_bf16_peak_algorithmic": round(tf_a / PEAK_BF16_TFLOPS, 4),
+                        "tflops_executed": round(tf_x, 1), "frac_bf16_peak_executed": round(tf_x / PEAK_BF16_TFLOPS, 4)})
         else:
             gbs = kern_bytes[name] / (ms * 1e-3) / 1e9
             ent.update({"gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)})
         kernels[name] = ent
     dom = max(("fwd", "dkdv", "dq", "delta"), key=lambda n: timer.avg_ms(n))
     dom_ms = timer.avg_ms(dom)
-    if dom in kern_flops:
-        ach = kern_flops[dom] / (dom_ms * 1e-3) / 1e12
+    if dom in exec_units:
+        ach = algo_units[dom] * nqnkd / (dom_ms * 1e-3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": _traffic(dom)}
     else:
@@ -214,6 +228,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and args.only is None:
         cpu = _cpu_baseline(w3, args.cpu_heads)
+        cpu["per_config"] = _cpu_per_config(workloads, legs)
 
     out = {
         "metric": METRIC,
@@ -307,6 +322,8 @@ def _time_graph(torch, fn, calls, reps=5):
 
 def _legs(torch, fa2, workloads, dev, only=None):
     legs = {}
+    if only in (None, "c1"):
+        _leg_c1(torch, fa2, workloads, dev, legs)
     if only in (None, "c3_fwd"):
         _leg_c3(torch, fa2, workloads, dev, legs)
     if only in (None, "c4"):
@@ -319,78 +336,7 @@ def _legs(torch, fa2, workloads, dev, only=None):
         _leg_decode(torch, fa2, workloads, dev, legs)
     if only in (None, "gemm_ref"):
         _leg_gemm_ref(torch, dev, legs)
-    if only == "vendor_ref":  # not in the default run: times a third-party kernel
-        _leg_vendor_ref(torch, fa2, workloads, dev, legs)
     return legs
-
-
-def _leg_vendor_ref(torch, fa2, workloads, dev, legs):
-    """torch's scaled_dot_product_attention with its flash backend forced (no
-    fallback to the composed math path) beside this library, same inputs:
-    the C3 and C4 forwards and the C5 backward (autograd through the flash
-    backward, timed from the saved forward). Reference context only."""
-    from torch.nn.attention import SDPBackend, sdpa_kernel
-
-    def timed(fn, reps=6):
-        fn()
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(reps):
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record()
-            fn()
-            e.record()
-            torch.cuda.synchronize()
-            ts.append(s.elapsed_time(e))
-        ts.sort()
-        return ts[len(ts) // 2]
-
-    def sdpa(q, k, v):
-        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
-            return torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=None)
-
-    out = {}
-    try:
-        for name, w, heads in (("c3_fwd", workloads.C3, 32), ("c4_fwd", workloads.C4, 16)):
-            x = workloads.attn_inputs(w, device=dev)
-            b = w.bh // heads
-            q4, k4, v4 = (x[t].view(b, heads, -1, w.head_dim) for t in ("q", "k", "v"))
-            o_v = sdpa(q4, k4, v4)
-            o, lse = fa2.fa2_fwd(x["q"], x["k"], x["v"], w.scale)
-            torch.cuda.synchronize()
-            diff = (o_v.reshape(o.shape).float() - o.float()).abs().max().item()
-            del o_v
-            tv = timed(lambda: sdpa(q4, k4, v4))
-            to = timed(lambda: fa2.fa2_fwd(x["q"], x["k"], x["v"], w.scale, o, lse))
-            fl = w.fwd_flops()
-            out[name] = {"vendor_ms": round(tv, 4), "vendor_tflops": round(fl / tv / 1e9, 1), "ours_ms": round(to, 4),
-                         "ours_tflops": round(fl / to / 1e9, 1), "max_abs_diff_o": diff}
-            del x, q4, k4, v4, o, lse
-            torch.cuda.empty_cache()
-        w = workloads.C5
-        x = workloads.attn_inputs(w, device=dev)
-        heads = 32
-        q4, k4, v4, do4 = (x[t].view(w.bh // heads, heads, w.n_q, w.head_dim) for t in ("q", "k", "v", "do"))
-        qr, kr, vr = (t.clone().requires_grad_(True) for t in (q4, k4, v4))
-        o_v = sdpa(qr, kr, vr)
-        o, lse = fa2.fa2_fwd(x["q"], x["k"], x["v"], w.scale)
-        grads = torch.autograd.grad(o_v, (qr, kr, vr), do4, retain_graph=True)
-        ours = fa2.attention_bwd(x["q"], x["k"], x["v"], o, x["do"], lse, w.scale)
-        torch.cuda.synchronize()
-        diff = max((g.reshape(m.shape).float() - m.float()).abs().max().item() for g, m in zip(grads, ours))
-        del grads, ours
-        tv = timed(lambda: torch.autograd.grad(o_v, (qr, kr, vr), do4, retain_graph=True))
-        to = timed(lambda: fa2.attention_bwd(x["q"], x["k"], x["v"], o, x["do"], lse, w.scale))
-        fl = w.bwd_flops()
-        out["c5_bwd"] = {"vendor_ms": round(tv, 4), "vendor_tflops_counted": round(fl / tv / 1e9, 1),
-                         "ours_ms": round(to, 4), "ours_tflops_counted": round(fl / to / 1e9, 1),
-                         "max_abs_diff_grads": diff}
-        del x, q4, k4, v4, do4, qr, kr, vr, o_v, o, lse
-        torch.cuda.empty_cache()
-    except RuntimeError as e:  # the flash backend is not available on this build
-        out["error"] = str(e)[:200]
-    legs["vendor_ref"] = out
-    print(f"[bench] leg vendor_ref {out}", file=sys.stderr, flush=True)
 
 
 def _leg_decode(torch, fa2, workloads, dev, legs):
@@ -443,6 +389,22 @@ def _leg_gemm_ref(torch, dev, legs):
     del a, b, c
     torch.cuda.empty_cache()
     print(f"[bench] leg gemm_ref {legs['gemm_ref']}", file=sys.stderr, flush=True)
+
+
+def _leg_c1(torch, fa2, workloads, dev, legs):
+    """Tiny float32 forward (BH 2, N 64, D 32): launch-bound; per call alone
+    (events around one call) and back to back (200 calls between two
+    events)."""
+    w1 = workloads.C1
+    x = workloads.attn_inputs(w1, device=dev)
+    o = torch.empty_like(x["q"])
+    lse = torch.empty((w1.bh, w1.n_q), dtype=torch.float32, device=dev)
+    ms = _time_fn(torch, lambda: fa2.fa2_fwd(x["q"], x["k"], x["v"], w1.scale, o, lse), 50)
+    ms_stream = _time_batch(torch, lambda: fa2.fa2_fwd(x["q"], x["k"], x["v"], w1.scale, o, lse), 200)
+    legs["c1"] = {"us_per_call": round(ms * 1e3, 2), "us_per_call_stream": round(ms_stream * 1e3, 2),
+                  "gflops_stream": round(w1.fwd_flops() / (ms_stream * 1e-3) / 1e9, 2)}
+    del x, o, lse
+    print(f"[bench] leg c1 {legs['c1']}", file=sys.stderr, flush=True)
 
 
 def _leg_c3(torch, fa2, workloads, dev, legs):
@@ -586,6 +548,56 @@ def _cpu_baseline(w, heads_arg):
                       f"(n_q = n_k = {w.n_q}, head_dim {w.head_dim}), bf16-rounded inputs upcast to fp64; "
                       f"{secs:.1f} s",
             "seconds": round(secs, 2), "cpu_model": cpu_model, "host": platform.node()}
+
+
+def _cpu_per_config(workloads, legs):
+    """The fp64 oracle per configuration on the host cores, beside the same
+    configuration's GPU time from the legs: C1 and C2 on their full inputs,
+    C3, C4 (forward) and C5 (backward) on the first few heads at full
+    length. Speed-up = oracle seconds per head / GPU seconds per head."""
+    import oracle
+
+    threads = oracle.default_threads()
+    out = {}
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    w = workloads.C1
+    x = workloads.attn_inputs(w, device="cpu")
+    secs = timed(lambda: oracle.attention_fwd(x["q"], x["k"], x["v"], w.scale, threads))
+    gpu_ms = legs.get("c1", {}).get("us_per_call", 0) / 1e3
+    out["c1"] = {"sample": "full input", "oracle_s": round(secs, 5), "gpu_ms": gpu_ms or None,
+                 "speedup": round(secs / (gpu_ms * 1e-3), 1) if gpu_ms else None}
+    w = workloads.C2
+    qkv = workloads.psa_inputs(w, device="cpu")
+    secs = timed(lambda: oracle.psa_block(qkv, w.num_heads, w.key_dim, threads))
+    gpu_ms = legs.get("c2", {}).get("us_per_call_warm", 0) / 1e3
+    gpu_fused = legs.get("c2", {}).get("fused_us_per_call_warm", 0) / 1e3
+    out["c2"] = {"sample": "full input (pack, attention on V_lo and V_hi, merge)", "oracle_s": round(secs, 4),
+                 "gpu_ms_block": gpu_ms or None, "gpu_ms_fused": gpu_fused or None,
+                 "speedup_block": round(secs / (gpu_ms * 1e-3), 1) if gpu_ms else None,
+                 "speedup_fused": round(secs / (gpu_fused * 1e-3), 1) if gpu_fused else None}
+    for name, w, heads, bwd, leg, key in (("c3", workloads.C3, 8, False, "c3_fwd", "ms"),
+                                          ("c4", workloads.C4, 16, False, "c4", "ms"),
+                                          ("c5", workloads.C5, 8, True, "c5", "ms")):
+        x = workloads.attn_inputs(w, device="cpu", bh=heads, with_do=bwd, seed=w.seed)
+        if bwd:  # the oracle's backward recomputes P from Q, K, V itself
+            secs = timed(lambda: oracle.attention_bwd(x["q"], x["k"], x["v"], x["do"], w.scale, threads))
+        else:
+            secs = timed(lambda: oracle.attention_fwd(x["q"], x["k"], x["v"], w.scale, threads))
+        gpu_ms = legs.get(leg, {}).get(key)
+        per_head_gpu = gpu_ms * 1e-3 / w.bh if gpu_ms else None
+        fl = (w.bwd_flops() if bwd else w.fwd_flops()) * heads / w.bh
+        out[name] = {"sample": f"{heads} of {w.bh} heads at full length" + (" (backward)" if bwd else " (forward)"),
+                     "oracle_s": round(secs, 3), "oracle_gflops": round(fl / secs / 1e9, 2),
+                     "gpu_ms_all_heads": gpu_ms,
+                     "speedup": round((secs / heads) / per_head_gpu, 1) if per_head_gpu else None}
+    out["threads"] = threads
+    print(f"[bench] oracle per config {out}", file=sys.stderr, flush=True)
+    return out
 
 
 if __name__ == "__main__":
