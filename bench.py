@@ -62,6 +62,9 @@ def _parse():
     ap.add_argument("--only", choices=["main", "c1", "c3_fwd", "c4", "c5", "c2", "decode", "gemm_ref"], default=None,
                     help="run just the main step or just one leg (for profiling one workload); prints no JSON "
                          "line unless it is the main step")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
+                    help="no GPU: read the rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE outputs (run_counter_collection.csv "
+                         "of a run with --calibrate-copy) and write profiles/traffic.json")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run a plain 1 GiB device copy three times (reference kernel "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -119,8 +122,70 @@ def _flush_buffer(torch):
     return torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
 
 
+# kernels of the step (rocprofv3 kernel names, template arguments as printed)
+# and the sources their code comes from
+TRAFFIC_KERNELS = {
+    "fwd": ("fwd_kernel<(fa2mi::Dt)2, 128, 64, 8, false>", ["attention_fa2_fwd_02_amd/csrc/fa2_fwd.hip"]),
+    "dkdv": ("dkdv_kernel<(fa2mi::Dt)2, 128, 32, 8>", ["attention_fa2_fwd_02_amd/csrc/fa2_bwd.hip"]),
+    "dq": ("dq_kernel<(fa2mi::Dt)2, 128, 64, 8>", ["attention_fa2_fwd_02_amd/csrc/fa2_bwd.hip"]),
+    "delta": ("delta_kernel<(fa2mi::Dt)2, 128>", ["attention_fa2_fwd_02_amd/csrc/fa2_bwd.hip"]),
+}
+
+
+def _write_traffic(fetch_dir: str, write_dir: str):
+    """profiles/traffic.json from two rocprofv3 counter runs of the step with
+    --calibrate-copy: each counter's KiB per dispatch, scaled by what the same
+    counter reads for the plain 1 GiB device copy of the same program."""
+    import csv
+    from collections import defaultdict
+
+    def per_kernel(d):
+        f = next(Path(d).rglob("*counter_collection.csv"))
+        agg = defaultdict(list)
+        for r in csv.DictReader(open(f)):
+            agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in agg.items()}
+
+    fetch, write = per_kernel(fetch_dir), per_kernel(write_dir)
+    copy = [k for k in fetch if "copyBuffer" in k or "__amd_rocclr_copy" in k]
+    if not copy:
+        raise SystemExit("no device copy kernel in the counter run (was it taken with --calibrate-copy?)")
+    ck = max(copy, key=lambda k: fetch[k])
+    sf, sw = 1048576.0 / fetch[ck], 1048576.0 / write[ck]
+    out = {"what": "HBM bytes per launch of each kernel of the LLM-shape step (BH 512, N 4096, D 128, bf16), from "
+                   "rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by the factor that maps the same "
+                   "counter on a plain 1 GiB device copy to 1 GiB",
+           "command_fetch": "rocprofv3 --pmc FETCH_SIZE -d <fetch_dir> -o run --output-format csv -- python3 bench.py "
+                            "--steps 3 --warmup 1 --no-legs --no-cpu-baseline --calibrate-copy",
+           "command_write": "rocprofv3 --pmc WRITE_SIZE -d <write_dir> -o run --output-format csv -- python3 bench.py "
+                            "--steps 3 --warmup 1 --no-legs --no-cpu-baseline --calibrate-copy",
+           "command_summary": "python3 bench.py --write-traffic <fetch_dir> <write_dir>",
+           "copy_reference_kib": {"FETCH_SIZE": round(fetch[ck], 4), "WRITE_SIZE": round(write[ck], 4),
+                                  "bytes": 1 << 30},
+           "scale": {"fetch": round(sf, 4), "write": round(sw, 4)}, "kernels": {}}
+    for key, (name, srcs) in TRAFFIC_KERNELS.items():
+        srcs = srcs + ["attention_fa2_fwd_02_amd/csrc/fa2_device.h"]
+        fk = [k for k in fetch if k.startswith("fa2mi::" + name) or name in k]
+        wk = [k for k in write if k.startswith("fa2mi::" + name) or name in k]
+        if not fk or not wk:
+            raise SystemExit(f"kernel {name} not found in the counter runs")
+        fr, wr = fetch[fk[0]], write[wk[0]]
+        h = hashlib.sha256()
+        for src in srcs:
+            h.update((ROOT / src).read_bytes())
+        out["kernels"][key] = {"kernel": name, "fetch_kib_raw": round(fr, 1), "write_kib_raw": round(wr, 1),
+                               "fetch_bytes": int(fr * 1024 * sf), "write_bytes": int(wr * 1024 * sw),
+                               "source": srcs, "source_sha256": h.hexdigest()}
+    (ROOT / "profiles" / "traffic.json").write_text(json.dumps(out, indent=1) + "\n")
+    for key, ent in out["kernels"].items():
+        print(key, ent["fetch_bytes"] / 1e9, ent["write_bytes"] / 1e9)
+
+
 def main():
     args = _parse()
+    if args.write_traffic:
+        _write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards over heads with no "
               "exchange, so per-GPU throughput is the N=1 figure. Nothing was run.", file=sys.stderr)
