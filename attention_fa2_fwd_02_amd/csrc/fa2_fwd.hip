@@ -329,7 +329,13 @@ __device__ __forceinline__ void fwd_pass_dma(__amdgpu_buffer_rsrc_t krs, __amdgp
 // recurrence (row max on every tile, lazy rescaling) in one pass. After each
 // tile the next tile, already in registers, is stored into the other stage
 // and the one after is fetched; one barrier per tile orders this tile's reads
-// of a stage before that stage is refilled two tiles later.
+// of a stage before that stage is refilled two tiles later. (float32 does
+// not take the two-pass form of the 16-bit types: compiled that way, the
+// first P V product of a pass read its accumulator input from a separate
+// register block that the next LDS load and VALU results overwrote within
+// 0-15 issue slots while the 16-pass f32 MFMA was still reading it, which
+// corrupted output channels 16-23; tests/test_isa_srcc_war.py scans every
+// kernel for that pattern.)
 template <int D, int WAVES>
 __device__ __forceinline__ void fwd_pass_f32(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
                                              const float (&qf)[D / 2], f32x16 (&acc)[D / 32], float &m_ref,
