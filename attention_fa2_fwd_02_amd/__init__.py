@@ -307,7 +307,10 @@ def psa_merge_attn(o_lo, o_hi, batch: int, num_heads: int, h: int, w: int, out=N
 def psa_block(qkv, num_heads: int, key_dim: int, workspace: dict | None = None):
     """PSA attention block: pack -> fa2_fwd(Q, K, V_lo) -> fa2_fwd(Q, K, V_hi)
     -> merge, at scale 1/sqrt(key_dim). ``workspace`` (optional dict) keeps
-    the intermediate buffers between calls of the same shape."""
+    the intermediate buffers between calls of the same shape. With a
+    workspace the returned tensor is ``workspace["out"]``: it belongs to the
+    workspace and the next call with the same workspace overwrites it (clone
+    it to keep it); without one every call returns a fresh tensor."""
     b, _, h, w = qkv.shape
     ws = workspace if workspace is not None else {}
     shape_key = (tuple(qkv.shape), qkv.dtype, qkv.device, num_heads, key_dim)
@@ -416,7 +419,10 @@ def psa_block_backward(d_out, num_heads: int, key_dim: int, workspace: dict):
     operands, both attention outputs and the LSE); the backward's own buffers
     are kept in it too. Steps: merge backward -> for V_lo and V_hi: delta,
     dK/dV, dQ on the packed sections -> pack backward, which adds the second
-    call's dQ and dK to the first's. Returns d_qkv [B, nh*4*kd, H, W]."""
+    call's dQ and dK to the first's. Returns d_qkv [B, nh*4*kd, H, W], which
+    is ``workspace["d_qkv"]``: it belongs to the workspace and the next
+    backward call with the same workspace overwrites it (clone it to keep
+    it)."""
     ws = workspace
     _check("d_out", d_out)
     b, ch, h, w = d_out.shape
