@@ -48,15 +48,6 @@ template <> struct Traits<Dt::BF16> {
     __device__ static inline f32x16 mfma(frag a, frag b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
-    // acc + the sum of the fragment's 8 elements (fp32 accumulation)
-    __device__ static inline float sum_frag(frag f, float acc) {
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 0, 1), one, acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 2, 3), one, acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 4, 5), one, acc, false);
-        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 6, 7), one, acc, false);
-    }
 };
 
 template <> struct Traits<Dt::F16> {
@@ -66,15 +57,6 @@ template <> struct Traits<Dt::F16> {
     static constexpr int KPL = 8;
     __device__ static inline f32x16 mfma(frag a, frag b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-    }
-    // acc + the sum of the fragment's 8 elements (fp32 accumulation)
-    __device__ static inline float sum_frag(frag f, float acc) {
-        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-        const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
-        acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(f, f, 0, 1), one, acc, false);
-        acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(f, f, 2, 3), one, acc, false);
-        acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(f, f, 4, 5), one, acc, false);
-        return __builtin_amdgcn_fdot2(__builtin_shufflevector(f, f, 6, 7), one, acc, false);
     }
 };
 
@@ -88,6 +70,21 @@ template <> struct Traits<Dt::F32> {
     }
     __device__ static inline float sum_frag(frag f, float acc) { return acc + f; }
 };
+
+// Sum of the 16 values of a C block, as a balanced tree so that the adds
+// overlap. Row sums of probabilities use plain float adds: on gfx950 a packed
+// dot (v_dot2c_f32_bf16 / _f16, the other way to sum 16-bit pairs) does not
+// issue while the matrix pipe runs, and each one was measured to add about
+// 7.5 cycles to a wave's MFMA stream, where independent float adds hide
+// under it.
+__device__ __forceinline__ float sum16(const f32x16 &c) {
+    float a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = c[2 * i] + c[2 * i + 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = a[2 * i] + a[2 * i + 1];
+    return (a[0] + a[1]) + (a[2] + a[3]);
+}
 
 // Row of C-block register c for lane half h.
 __device__ __forceinline__ constexpr int crow(int c, int h) { return 8 * (c >> 2) + 4 * h + (c & 3); }

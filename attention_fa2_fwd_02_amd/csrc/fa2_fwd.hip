@@ -10,9 +10,9 @@
 //   2. S^T = K Q^T on MFMA: one C block per 32 keys; each lane owns one query
 //      (the C column), so a row's max needs one exchange between lane halves.
 //   3. Online softmax in the log2 domain (scale*log2(e) folded into one FMA
-//      before exp2): P = 2^(S - m), l += rowsum(P) over P as rounded to the
-//      element type for the product (lane-partial sums, combined at the
-//      end). The reference m is the first tile's row max; later tiles use
+//      before exp2): P = 2^(S - m), l += rowsum(P) in float32 over P before
+//      it is rounded to the element type for the product (lane-partial
+//      sums, combined at the end). The reference m is the first tile's row max; later tiles use
 //      it as it is unless l leaves range, in which case the workgroup redoes
 //      the rows with the max taken on every tile and m raised lazily (only
 //      when a row max exceeds it by more than kRescaleLog2, O and l then
@@ -152,9 +152,8 @@ __device__ __forceinline__ void fwd_tile(const typename Traits<DT>::elem *kt, co
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int c = 0; c < 16; ++c) s[kb][c] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][c], scale_log2, neg_m));
-    // O^T += V^T P^T: per 16-key step, one P fragment feeds all d blocks.
-    // l sums the probabilities as rounded for the product (so O = acc / l
-    // normalises exactly the weights applied).
+    // O^T += V^T P^T: per 16-key step, one P fragment feeds all d blocks;
+    // l sums the probabilities.
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -223,12 +222,14 @@ __device__ __forceinline__ void fwd_tile_dma(const char *kt, const char *vt, con
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int c = 0; c < 16; ++c) s[kb][c] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][c], scale_log2, neg_m));
+    // l: float32 sum of the probabilities before they are rounded for the
+    // product
+    l_run += sum16(s[0]) + sum16(s[1]);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int t = 0; t < TP; ++t) {
             const frag pf = c_to_frag<DT>(s[kb], t);
-            l_run = Tr::sum_frag(pf, l_run);
 #pragma unroll
             for (int db = 0; db < NDB; ++db) acc[db] = Tr::mfma(sw.vt(vt, kb, t, db), pf, acc[db]);
         }
@@ -309,18 +310,103 @@ __device__ __forceinline__ void fwd_pass_dma(__amdgpu_buffer_rsrc_t krs, __amdgp
             step(std::false_type{}, std::false_type{}, it + 1);
         }
         if (it < nfull) step(std::false_type{}, std::true_type{}, it++);
+        // ragged last tile: the first and only one sets the reference max;
+        // after full tiles pass 0 keeps the reference (no rescaling, which
+        // could shrink an l that already exceeded the limit back under it)
         if (nfull < ntiles) {
-            if (nfull & 1)
-                fwd_tile_dma<DT, D, true, false, true>(K1, V1, sw, qf, acc, m_ref, l_run, scale_log2,
-                                                       klen - nfull * BC, lane);
-            else
-                fwd_tile_dma<DT, D, true, false, true>(K0, V0, sw, qf, acc, m_ref, l_run, scale_log2,
-                                                       klen - nfull * BC, lane);
+            const int kv = klen - nfull * BC;
+            if (FASTP && nfull > 0) {
+                if (nfull & 1) fwd_tile_dma<DT, D, true, true, false>(K1, V1, sw, qf, acc, m_ref, l_run, scale_log2, kv, lane);
+                else fwd_tile_dma<DT, D, true, true, false>(K0, V0, sw, qf, acc, m_ref, l_run, scale_log2, kv, lane);
+            } else {
+                if (nfull & 1) fwd_tile_dma<DT, D, true, false, true>(K1, V1, sw, qf, acc, m_ref, l_run, scale_log2, kv, lane);
+                else fwd_tile_dma<DT, D, true, false, true>(K0, V0, sw, qf, acc, m_ref, l_run, scale_log2, kv, lane);
+            }
         }
     };
-    run_pass(std::true_type{});
+    if constexpr (WAVES == 8) {
+        // Pass 0 of 8-wave workgroups with tiles fetched two ahead: three LDS
+        // stages (tile t in stage t % 3); step t issues the DMA of tile t + 2
+        // into the stage of tile t - 1 (last read before the previous
+        // barrier), computes tile t, then waits for tile t + 1's pieces only
+        // (loads complete in order) and meets the others at the barrier.
+        __shared__ __attribute__((aligned(1024))) char K2[BYTES];
+        __shared__ __attribute__((aligned(1024))) char V2[BYTES];
+        using F = std::false_type;
+        using T = std::true_type;
+        // DMA instructions per wave and tile (a wave with no piece has none
+        // outstanding, so the count holds for every wave)
+        constexpr int NPW = 2 * ((PIECES + WAVES - 1) / WAVES);
+        static_assert((PIECES % WAVES == 0 || PIECES < WAVES) && NPW < 16, "pieces per wave");
+        auto kst = [&](auto st) -> char * {
+            constexpr int S = decltype(st)::value;
+            if constexpr (S == 0) return K0;
+            else if constexpr (S == 1) return K1;
+            else return K2;
+        };
+        auto vst = [&](auto st) -> char * {
+            constexpr int S = decltype(st)::value;
+            if constexpr (S == 0) return V0;
+            else if constexpr (S == 1) return V1;
+            else return V2;
+        };
+#pragma unroll
+        for (int i = 0; i < NDB; ++i) acc[i] = zero16();
+        m_ref = -INFINITY;
+        l_run = 0.f;
+        dma_tile(0, K0, V0);
+        dma_tile(1, K1, V1);
+        __builtin_amdgcn_s_waitcnt(0x0f70 | NPW);  // tile 0 landed
+        lds_changed();
+        __builtin_amdgcn_s_barrier();
+        lds_changed();
+        auto step = [&](auto first_tag, auto stage_tag, int it) {
+            constexpr int S = decltype(stage_tag)::value;
+            using S2N = std::integral_constant<int, (S + 2) % 3>;
+            dma_tile(it + 2, kst(S2N{}), vst(S2N{}));
+            __builtin_amdgcn_sched_barrier(0);
+            fwd_tile_dma<DT, D, false, true, decltype(first_tag)::value>(kst(stage_tag), vst(stage_tag), sw, qf, acc,
+                                                                         m_ref, l_run, scale_log2, BC, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            // tile it + 1 landed (this wave's pieces; tile it + 2 stays in
+            // flight), then a bare barrier: __syncthreads' release fence
+            // would drain every outstanding DMA, tile it + 2's included. LDS
+            // is written here only by the DMA, so no other store needs it.
+            __builtin_amdgcn_s_waitcnt(0x0f70 | NPW);
+            lds_changed();
+            __builtin_amdgcn_s_barrier();
+            lds_changed();
+        };
+        using S0 = std::integral_constant<int, 0>;
+        using S1 = std::integral_constant<int, 1>;
+        using S2 = std::integral_constant<int, 2>;
+        int it = 0;
+        if (nfull > 0) step(T{}, S0{}, it++);
+        for (; it + 2 < nfull; it += 3) {
+            step(F{}, S1{}, it);
+            step(F{}, S2{}, it + 1);
+            step(F{}, S0{}, it + 2);
+        }
+        if (it < nfull) step(F{}, S1{}, it++);
+        if (it < nfull) step(F{}, S2{}, it++);
+        if (nfull < ntiles) {
+            const int st = nfull % 3;
+            const int kv = klen - nfull * BC;
+            if (nfull == 0) fwd_tile_dma<DT, D, true, false, true>(K0, V0, sw, qf, acc, m_ref, l_run, scale_log2, kv, lane);
+            else if (st == 0) fwd_tile_dma<DT, D, true, true, false>(K0, V0, sw, qf, acc, m_ref, l_run, scale_log2, kv, lane);
+            else if (st == 1) fwd_tile_dma<DT, D, true, true, false>(K1, V1, sw, qf, acc, m_ref, l_run, scale_log2, kv, lane);
+            else fwd_tile_dma<DT, D, true, true, false>(K2, V2, sw, qf, acc, m_ref, l_run, scale_log2, kv, lane);
+        }
+        wait_dma();  // nothing left in flight past the pass
+    } else {
+        run_pass(std::true_type{});
+    }
     // a barrier for the whole workgroup either way: pass 1 refills the stages
-    const bool bad = !(l_run <= 0x1p100f);  // also true for inf and NaN
+    // l sums the float32 probabilities, so it bounds every one of them: at
+    // or below the limit none overflowed the element type when rounded for
+    // the product (f16 tops out at 65504, bf16 near 2^128)
+    constexpr float kLim = DT == Dt::F16 ? 65504.f : 0x1p100f;
+    const bool bad = !(l_run <= kLim);  // also true for inf and NaN
     if (__syncthreads_or(bad)) run_pass(std::false_type{});
 }
 
@@ -444,15 +530,17 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     const uint32_t head_bytes = (uint32_t)klen * D * (uint32_t)sizeof(elem);
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + koff, head_bytes);
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + koff, head_bytes);
-    // Pass 0 (16-bit types) takes the row max on the first tile (and on a
-    // ragged last one) only: later probabilities are 2^(s - m_ref) against
+    // Pass 0 (16-bit types) takes the row max on the first tile only: later
+    // probabilities (a ragged last tile's included) are 2^(s - m_ref) against
     // that reference as they are. The reference only scales every
     // probability of a row by the same power of two, which O = acc / l
     // cancels, so this is the same softmax as long as the values stay in
-    // range. If some row of the workgroup ends with l above 2^100 or not
-    // finite (a score about 100 or more above the first tile's max, in log2
-    // units), the workgroup runs pass 1: the recurrence with the max taken on
-    // every tile (lazy rescaling). float32 runs that exact recurrence only.
+    // range. If some row of the workgroup ends with l above 2^100 (bf16) or
+    // 65504 (f16, where a probability above it would not fit the element
+    // type of the product) or not finite (a score about 100, or for f16 16,
+    // or more above the first tile's max, in log2 units), the workgroup runs
+    // pass 1: the recurrence with the max taken on every tile (lazy
+    // rescaling). float32 runs that exact recurrence only.
     if constexpr (TR)
         fwd_pass_dma<DT, D, WAVES>(krs, vrs, qf, acc, m_ref, l_run, scale_log2, klen, lane, wave);
     else

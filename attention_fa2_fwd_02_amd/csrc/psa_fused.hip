@@ -440,8 +440,8 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, KS
     __syncthreads();
     if (active) {
         // probabilities block by block, so that the exp2 of a block overlaps
-        // the P V products of the one before; the row sum is taken over the
-        // rounded probabilities the products use
+        // the P V products of the one before; the row sum is taken in float32
+        // over the probabilities before they are rounded for the products
         // (a slice with no keys keeps m = -inf and contributes nothing)
         const float neg_m = m == -INFINITY ? 0.f : -m;
 #pragma unroll
@@ -449,10 +449,10 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, KS
             if (kb >= nb) break;
 #pragma unroll
             for (int c = 0; c < 16; ++c) s[kb][c] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][c], scale_log2, neg_m));
+            l_run += sum16(s[kb]);
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const frag pf = c_to_frag<DT>(s[kb], t);
-                l_run = Tr::sum_frag(pf, l_run);
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
                     acc[db] = Tr::mfma(ld_t_frag<DT>(Vt + (32 * db + col) * LDVT, kb0 + kb, t, h), pf, acc[db]);
