@@ -481,6 +481,18 @@ def _leg_c3(torch, fa2, workloads, dev, legs):
     ms = _time_fn(torch, lambda: fa2.fa2_fwd(x["q"], x["k"], x["v"], w3.scale, o, lse), 10)
     tf = w3.fwd_flops() / (ms * 1e-3) / 1e12
     legs["c3_fwd"] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    # Context, not a result: the same launch on constant inputs (Q = K =
+    # 0.25, V = 0.5). The kernel runs the same instructions in the same
+    # number of cycles whatever the data; what changes is the clock the chip
+    # holds, which drops with the switching power of random operands. The
+    # ratio of the two times is that clock ratio.
+    for t, val in ((x["q"], 0.25), (x["k"], 0.25), (x["v"], 0.5)):
+        t.fill_(val)
+    ms_c = _time_fn(torch, lambda: fa2.fa2_fwd(x["q"], x["k"], x["v"], w3.scale, o, lse), 10)
+    tf_c = w3.fwd_flops() / (ms_c * 1e-3) / 1e12
+    legs["c3_fwd"].update({"const_inputs_ms": round(ms_c, 4), "const_inputs_tflops": round(tf_c, 1),
+                           "const_inputs_frac_bf16_peak": round(tf_c / PEAK_BF16_TFLOPS, 4),
+                           "clock_ratio_const_over_random": round(ms / ms_c, 3)})
     del x, o, lse
     torch.cuda.empty_cache()
     print(f"[bench] leg c3_fwd {legs['c3_fwd']}", file=sys.stderr, flush=True)
