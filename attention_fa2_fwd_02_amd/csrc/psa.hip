@@ -71,8 +71,11 @@ __global__ __launch_bounds__(256) void to_rows_kernel(const elem *__restrict__ s
     __shared__ __attribute__((aligned(16))) elem tile[KD * LD];
 
     const int tid = threadIdx.x;
-    const int slice = blockIdx.x / tiles_per_slice;
-    const int p0 = (blockIdx.x % tiles_per_slice) * P;
+    // neighbouring tiles of a slice share cache lines at their edges (a
+    // channel row is rarely a multiple of 128 bytes): keep them on one XCD
+    const int b = xcd_remap(blockIdx.x, gridDim.x);
+    const int slice = b / tiles_per_slice;
+    const int p0 = (b % tiles_per_slice) * P;
     const int s = slice % NSEC, bhh = slice / NSEC;
     const elem *src = src_all + (int64_t)slice * KD * hw;
     elem *dst = const_cast<elem *>(static_cast<const elem *>(dst_sec.p[s])) + (int64_t)bhh * hw * KD;
@@ -114,8 +117,11 @@ __global__ __launch_bounds__(256) void to_channels_kernel(SecPtrs src_sec, SecPt
     __shared__ __attribute__((aligned(16))) elem tile[P * LD];
 
     const int tid = threadIdx.x;
-    const int slice = blockIdx.x / tiles_per_slice;
-    const int p0 = (blockIdx.x % tiles_per_slice) * P;
+    // neighbouring tiles of a slice share cache lines at their edges (a
+    // channel row is rarely a multiple of 128 bytes): keep them on one XCD
+    const int b = xcd_remap(blockIdx.x, gridDim.x);
+    const int slice = b / tiles_per_slice;
+    const int p0 = (b % tiles_per_slice) * P;
     const int s = slice % NSEC, bhh = slice / NSEC;
     const elem *src = static_cast<const elem *>(src_sec.p[s]) + (int64_t)bhh * hw * KD;
     elem *dst = out + (int64_t)slice * KD * hw;
