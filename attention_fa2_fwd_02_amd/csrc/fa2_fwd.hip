@@ -192,11 +192,15 @@ __device__ __forceinline__ void fwd_tile_dma(const char *kt, const char *vt, con
         for (int t = 0; t < TS; ++t) s[kb] = Tr::mfma(sw.k(kt, kb, t), qf[t], s[kb]);
     }
     if constexpr (MASK) {
+        // key row of register c: 32 kb + crow(c, h) = 32 kb + 8 (c / 4) + c % 4
+        // + 4 h; one per-lane bound against constant offsets (no per-register
+        // row index to keep live)
+        const int kv = kvalid - 4 * h;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int c = 0; c < 16; ++c)
-                if (32 * kb + crow(c, h) >= kvalid) s[kb][c] = -INFINITY;
+                if (32 * kb + 8 * (c >> 2) + (c & 3) >= kv) s[kb][c] = -INFINITY;
     }
     if constexpr (!FAST || FIRST) {
         float mx = -INFINITY;
@@ -235,16 +239,97 @@ __device__ __forceinline__ void fwd_tile_dma(const char *kt, const char *vt, con
         }
 }
 
-// Both passes of the 16-bit forward (see fwd_kernel) on DMA-filled tiles.
-// Tiles go straight from memory into LDS (buffer -> LDS DMA, no register
-// staging) in two stages, each its own LDS array so that the compiler can
-// tell a stage being filled from the stage being read (it then keeps the DMA
-// in flight across the reads instead of waiting for it). Step it issues the
-// DMA of tile it + 1 into the other stage (last read in step it - 1, before
-// that step's barrier), computes tile it, then waits for its own DMA pieces
-// and meets the other waves at the tile's one barrier, which publishes tile
-// it + 1. Past the last tile the DMA reads zeros (buffer range check) into a
-// stage no later step reads.
+// Issues this wave's share of the DMA of K/V tile `tile` of a head (64 rows,
+// PIECES 1 KiB pieces per tile and tensor, piece J to wave J % WAVES) into
+// the stage arrays kd / vd. Bytes past the buffer's range read as zero.
+template <Dt DT, int D, int WAVES>
+__device__ __forceinline__ void fwd_dma_tile(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, int tile,
+                                             char *kd, char *vd, int wv, int lane) {
+    using Sw = SwzTile<DT, D>;
+    constexpr int BYTES = Sw::BYTES, PIECES = Sw::PIECES;
+    const uint32_t t0 = (uint32_t)tile * (uint32_t)BYTES;
+#pragma unroll
+    for (int j = 0; j < (PIECES + WAVES - 1) / WAVES; ++j) {
+        const int J = wv + WAVES * j;
+        if (PIECES % WAVES == 0 || J < PIECES) {
+            const uint32_t off = t0 + Sw::piece_off(J, lane);
+            dma16(krs, off, kd + 1024 * J);
+            dma16(vrs, off, vd + 1024 * J);
+        }
+    }
+}
+
+// One pass of the 16-bit forward over the key tiles of one head on two DMA
+// stages (tile it in K0/V0 for even it, K1/V1 for odd it), each stage its own
+// LDS array so that the compiler can tell a stage being filled from the
+// stage being read (it then keeps the DMA in flight across the reads instead
+// of waiting for it). Step it issues the DMA of tile it + 1 into the other
+// stage (last read in step it - 1, before that step's barrier), computes
+// tile it, then waits for its own DMA pieces and meets the other waves at
+// the tile's one barrier, which publishes tile it + 1. Past the last tile the
+// DMA reads zeros (buffer range check) into a stage no later step reads.
+// FASTP: pass 0 (reference max from the first tile); else the exact pass.
+template <Dt DT, int D, int WAVES, bool FASTP>
+__device__ __forceinline__ void fwd_pass2(char *K0, char *K1, char *V0, char *V1, __amdgpu_buffer_rsrc_t krs,
+                                          __amdgpu_buffer_rsrc_t vrs, const SwzTile<DT, D> &sw,
+                                          const typename Traits<DT>::frag (&qf)[D / 16], f32x16 (&acc)[D / 32],
+                                          float &m_ref, float &l_run, float scale_log2, int klen, int lane,
+                                          int wv) {
+    constexpr int BC = 64, NDB = D / 32;
+    const int ntiles = (klen + BC - 1) / BC;
+    const int nfull = klen / BC;
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) acc[i] = zero16();
+    m_ref = -INFINITY;
+    l_run = 0.f;
+    fwd_dma_tile<DT, D, WAVES>(krs, vrs, 0, K0, V0, wv, lane);
+    wait_dma();
+    __syncthreads();
+    lds_changed();
+    auto step = [&](auto first_tag, auto odd_tag, int it) {
+        constexpr bool FIRSTP = decltype(first_tag)::value;
+        constexpr bool ODD = decltype(odd_tag)::value;
+        // The scheduling barriers keep the DMA issue ahead of the tile and
+        // the wait for it behind the tile's last products (left to itself
+        // the compiler may sink the issue and hoist the wait, which then
+        // stalls on the DMA right away).
+        fwd_dma_tile<DT, D, WAVES>(krs, vrs, it + 1, ODD ? K0 : K1, ODD ? V0 : V1, wv, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        fwd_tile_dma<DT, D, false, FASTP, FIRSTP>(ODD ? K1 : K0, ODD ? V1 : V0, sw, qf, acc, m_ref, l_run,
+                                                   scale_log2, BC, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_dma();
+        __syncthreads();
+        lds_changed();
+    };
+    int it = 0;
+    if (nfull > 0) {
+        step(std::true_type{}, std::false_type{}, 0);
+        it = 1;
+    }
+    for (; it + 1 < nfull; it += 2) {
+        step(std::false_type{}, std::true_type{}, it);
+        step(std::false_type{}, std::false_type{}, it + 1);
+    }
+    if (it < nfull) step(std::false_type{}, std::true_type{}, it++);
+    // ragged last tile: the first and only one sets the reference max;
+    // after full tiles pass 0 keeps the reference (no rescaling, which
+    // could shrink an l that already exceeded the limit back under it)
+    if (nfull < ntiles) {
+        const int kv = klen - nfull * BC;
+        if (FASTP && nfull > 0) {
+            if (nfull & 1) fwd_tile_dma<DT, D, true, true, false>(K1, V1, sw, qf, acc, m_ref, l_run, scale_log2, kv, lane);
+            else fwd_tile_dma<DT, D, true, true, false>(K0, V0, sw, qf, acc, m_ref, l_run, scale_log2, kv, lane);
+        } else {
+            if (nfull & 1) fwd_tile_dma<DT, D, true, false, true>(K1, V1, sw, qf, acc, m_ref, l_run, scale_log2, kv, lane);
+            else fwd_tile_dma<DT, D, true, false, true>(K0, V0, sw, qf, acc, m_ref, l_run, scale_log2, kv, lane);
+        }
+    }
+}
+
+// Both passes of the 16-bit forward (see fwd_kernel) on DMA-filled tiles
+// (buffer -> LDS DMA, no register staging): fwd_pass2 on two stages, or for
+// 8-wave workgroups pass 0 on three stages with tiles fetched two ahead.
 template <Dt DT, int D, int WAVES>
 __device__ __forceinline__ void fwd_pass_dma(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
                                              const typename Traits<DT>::frag (&qf)[D / 16], f32x16 (&acc)[D / 32],
@@ -261,69 +346,7 @@ __device__ __forceinline__ void fwd_pass_dma(__amdgpu_buffer_rsrc_t krs, __amdgp
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     const int ntiles = (klen + BC - 1) / BC;
     const int nfull = klen / BC;
-    auto dma_tile = [&](int tile, char *kd, char *vd) {
-        const uint32_t t0 = (uint32_t)tile * (uint32_t)BYTES;
-#pragma unroll
-        for (int j = 0; j < (PIECES + WAVES - 1) / WAVES; ++j) {
-            const int J = wv + WAVES * j;
-            if (PIECES % WAVES == 0 || J < PIECES) {
-                const uint32_t off = t0 + Sw::piece_off(J, lane);
-                dma16(krs, off, kd + 1024 * J);
-                dma16(vrs, off, vd + 1024 * J);
-            }
-        }
-    };
-    auto run_pass = [&](auto fast_tag) {
-        constexpr bool FASTP = decltype(fast_tag)::value;
-#pragma unroll
-        for (int i = 0; i < NDB; ++i) acc[i] = zero16();
-        m_ref = -INFINITY;
-        l_run = 0.f;
-        dma_tile(0, K0, V0);
-        wait_dma();
-        __syncthreads();
-        lds_changed();
-        // stage of tile it: K0/V0 for even it, K1/V1 for odd it
-        auto step = [&](auto first_tag, auto odd_tag, int it) {
-            constexpr bool FIRSTP = decltype(first_tag)::value;
-            constexpr bool ODD = decltype(odd_tag)::value;
-            // The scheduling barriers keep the DMA issue ahead of the tile and
-            // the wait for it behind the tile's last products (left to itself
-            // the compiler may sink the issue and hoist the wait, which then
-            // stalls on the DMA right away).
-            dma_tile(it + 1, ODD ? K0 : K1, ODD ? V0 : V1);
-            __builtin_amdgcn_sched_barrier(0);
-            fwd_tile_dma<DT, D, false, FASTP, FIRSTP>(ODD ? K1 : K0, ODD ? V1 : V0, sw, qf, acc, m_ref, l_run,
-                                                       scale_log2, BC, lane);
-            __builtin_amdgcn_sched_barrier(0);
-            wait_dma();
-            __syncthreads();
-            lds_changed();
-        };
-        int it = 0;
-        if (nfull > 0) {
-            step(std::true_type{}, std::false_type{}, 0);
-            it = 1;
-        }
-        for (; it + 1 < nfull; it += 2) {
-            step(std::false_type{}, std::true_type{}, it);
-            step(std::false_type{}, std::false_type{}, it + 1);
-        }
-        if (it < nfull) step(std::false_type{}, std::true_type{}, it++);
-        // ragged last tile: the first and only one sets the reference max;
-        // after full tiles pass 0 keeps the reference (no rescaling, which
-        // could shrink an l that already exceeded the limit back under it)
-        if (nfull < ntiles) {
-            const int kv = klen - nfull * BC;
-            if (FASTP && nfull > 0) {
-                if (nfull & 1) fwd_tile_dma<DT, D, true, true, false>(K1, V1, sw, qf, acc, m_ref, l_run, scale_log2, kv, lane);
-                else fwd_tile_dma<DT, D, true, true, false>(K0, V0, sw, qf, acc, m_ref, l_run, scale_log2, kv, lane);
-            } else {
-                if (nfull & 1) fwd_tile_dma<DT, D, true, false, true>(K1, V1, sw, qf, acc, m_ref, l_run, scale_log2, kv, lane);
-                else fwd_tile_dma<DT, D, true, false, true>(K0, V0, sw, qf, acc, m_ref, l_run, scale_log2, kv, lane);
-            }
-        }
-    };
+    auto dma_tile = [&](int tile, char *kd, char *vd) { fwd_dma_tile<DT, D, WAVES>(krs, vrs, tile, kd, vd, wv, lane); };
     if constexpr (WAVES == 8) {
         // Pass 0 of 8-wave workgroups with tiles fetched two ahead: three LDS
         // stages (tile t in stage t % 3); step t issues the DMA of tile t + 2
@@ -399,7 +422,7 @@ __device__ __forceinline__ void fwd_pass_dma(__amdgpu_buffer_rsrc_t krs, __amdgp
         }
         wait_dma();  // nothing left in flight past the pass
     } else {
-        run_pass(std::true_type{});
+        fwd_pass2<DT, D, WAVES, true>(K0, K1, V0, V1, krs, vrs, sw, qf, acc, m_ref, l_run, scale_log2, klen, lane, wv);
     }
     // a barrier for the whole workgroup either way: pass 1 refills the stages
     // l sums the float32 probabilities, so it bounds every one of them: at
@@ -407,7 +430,9 @@ __device__ __forceinline__ void fwd_pass_dma(__amdgpu_buffer_rsrc_t krs, __amdgp
     // the product (f16 tops out at 65504, bf16 near 2^128)
     constexpr float kLim = DT == Dt::F16 ? 65504.f : 0x1p100f;
     const bool bad = !(l_run <= kLim);  // also true for inf and NaN
-    if (__syncthreads_or(bad)) run_pass(std::false_type{});
+    if (__syncthreads_or(bad))
+        fwd_pass2<DT, D, WAVES, false>(K0, K1, V0, V1, krs, vrs, sw, qf, acc, m_ref, l_run, scale_log2, klen, lane,
+                                       wv);
 }
 
 // The float32 forward: padded tiles staged through registers (K row-major,

@@ -92,6 +92,30 @@ def test_fwd_workgroup_sizes(dt, d, shape):
     _err("LSE", _np(lse), lse_ref, tol, case)
 
 
+@pytest.mark.parametrize("dt,mult", [("f16", 6.0), ("bf16", 16.0), ("bf16", 1.0), ("f16", 1.0)])
+def test_fwd_many_blocks_and_rerun(dt, mult):
+    """The 8-wave forward (three LDS stages, K/V fetched two tiles ahead) over
+    600 heads x 2 query blocks = 1200 workgroups, an uneven share per XCD,
+    with 200 keys (a ragged fourth tile). With mult > 1, every 7th head has
+    keys from 128 on equal to mult x its query 0, so that row's scores sit far
+    above the first tile's max: f16 overflows its probabilities at mult 6,
+    bf16 leaves range at mult 16, and the workgroups holding those rows redo
+    their block with the exact pass. Every output against the oracle."""
+    bh, nq, nk, d = 600, 300, 200, 64
+    case = f"many-block fwd {dt} x{mult}"
+    print(case, flush=True)
+    x = _inputs(dt, bh, nq, nk, d, seed=77)
+    k = x["k"].clone()
+    if mult != 1.0:
+        k[::7, 128:, :] = (mult * x["q"][::7, :1, :].float()).to(k.dtype)
+    o, lse = fa2.fa2_fwd(x["q"], k, x["v"])
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_fwd(x["q"], k, x["v"], 1 / math.sqrt(d))
+    tol = TOL[DTYPES[dt]]
+    _err("O", _np(o), o_ref, tol, case)
+    _err("LSE", _np(lse), lse_ref, tol, case)
+
+
 def test_fwd_c1_tiny_f32():
     w = workloads.C1
     x = workloads.attn_inputs(w, device=DEV)
@@ -535,8 +559,7 @@ def test_fwd_scores_far_above_first_tile(dt, mult):
     o_ref, lse_ref = oracle.attention_fwd(x["q"], k, x["v"], 1 / 8.0)
     tol = TOL[DTYPES[dt]]
     _err("O", _np(o), o_ref, tol, case)
-    # lse reaches a few hundred here: compare it relative to its size
-    _err("LSE", _np(lse), lse_ref, tol * max(1.0, float(np.abs(lse_ref).max()) / 8.0), case)
+    _err("LSE", _np(lse), lse_ref, tol, case)
 
 
 def test_fwd_degenerate_inputs_full_length():
