@@ -445,13 +445,47 @@ __device__ __forceinline__ void dkdv_pass_dma(__amdgpu_buffer_rsrc_t qrs, __amdg
 #pragma unroll
     for (int i = 0; i < NDB; ++i) accK[i] = accV[i] = zero16();
 
+    // One query tile. The operands come from LDS ahead of their products, in
+    // an order pinned by scheduling barriers: the Q, dO and V fragments of
+    // step t + 1 are read before the S and dP products of step t, and the
+    // transposed dO / Q fragment of dV / dK product i + 2 before product i
+    // (left to itself at 256 registers, the compiler reads each operand just
+    // before its product and waits for it, which left the matrix pipe idle
+    // about 40% of the time). The offsets are rebuilt from three base
+    // registers per tile to make room for the operands in flight.
     auto tile_fn = [&](const char *qt, const char *dt, const float *ls, const float *es) {
+        constexpr int AHEAD1 = 1, AHEAD2 = 2;
+        uint32_t k0 = sw.koff[0], v0 = sw.voff[0][0], v1 = sw.voff[0][1];
+        opaque(k0);
+        opaque(v0);
+        opaque(v1);
         f32x16 s = zero16(), dp = zero16();
+        frag qa[TS], da[TS], va[TS];
+        auto read1 = [&](int t) {
+            qa[t] = Sw::k_at(qt, k0, t);
+            da[t] = Sw::k_at(dt, k0, t);
+            va[t] = Sw::k_at(vown, k0, t);
+        };
+#pragma unroll
+        for (int t = 0; t < AHEAD1; ++t) read1(t);
 #pragma unroll
         for (int t = 0; t < TS; ++t) {
-            s = Tr::mfma(sw.k(qt, 0, t), kf[t], s);
-            dp = Tr::mfma(sw.k(dt, 0, t), sw.k(vown, 0, t), dp);
+            if (t + AHEAD1 < TS) read1(t + AHEAD1);
+            __builtin_amdgcn_sched_barrier(0);
+            s = Tr::mfma(qa[t], kf[t], s);
+            dp = Tr::mfma(da[t], va[t], dp);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        // A operands of the 4 NDB dV / dK products, i = 2 (NDB t + db) + (0: dV, 1: dK)
+        constexpr int NP = 4 * NDB;
+        frag ob[NP];
+        auto read2 = [&](int i) {
+            const int t = i / (2 * NDB), db = (i >> 1) % NDB;
+            ob[i] = Sw::vt_at((i & 1) ? qt : dt, v0, v1, t, db);
+        };
+#pragma unroll
+        for (int i = 0; i < AHEAD2; ++i) read2(i);
+        __builtin_amdgcn_sched_barrier(0);
         // p into s, dS into dp (rows = queries along a lane's registers)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -467,15 +501,19 @@ __device__ __forceinline__ void dkdv_pass_dma(__amdgpu_buffer_rsrc_t qrs, __amdg
                 dp[c] = pv * (dp[c] - dv[i]);
             }
         }
+        const frag pf[2] = {c_to_frag<DT>(s, 0), c_to_frag<DT>(s, 1)};
+        const frag dsf[2] = {c_to_frag<DT>(dp, 0), c_to_frag<DT>(dp, 1)};
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const frag pf = c_to_frag<DT>(s, t);
-            const frag dsf = c_to_frag<DT>(dp, t);
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                accV[db] = Tr::mfma(sw.vt(dt, 0, t, db), pf, accV[db]);
-                accK[db] = Tr::mfma(sw.vt(qt, 0, t, db), dsf, accK[db]);
-            }
+        for (int i = 0; i < NP; ++i) {
+            if (i + AHEAD2 < NP) read2(i + AHEAD2);
+            __builtin_amdgcn_sched_barrier(0);
+            const int t = i / (2 * NDB), db = (i >> 1) % NDB;
+            if (i & 1)
+                accK[db] = Tr::mfma(ob[i], dsf[t], accK[db]);
+            else
+                accV[db] = Tr::mfma(ob[i], pf[t], accV[db]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 

@@ -422,6 +422,22 @@ struct SwzTile {
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + voff[db][1]));
         return __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
+    // The same reads from the step-0 offsets alone: the chunk index of step t
+    // (or d block db) is that of step 0 XOR 2t (or 4 db), and the XOR only
+    // touches the chunk bits of the offset. A caller that passes koff[0] /
+    // voff[0][*] through opaque() once per tile keeps one register per base
+    // instead of TS + 2 NDB loop-invariant offsets.
+    __device__ static __forceinline__ frag k_at(const char *tile, uint32_t k0, int t) {
+        return *reinterpret_cast<const frag *>(tile + (k0 ^ (uint32_t)(t << 5)));
+    }
+    __device__ static __forceinline__ frag vt_at(const char *tile, uint32_t v0, uint32_t v1, int t, int db) {
+        typedef short i16x4 __attribute__((ext_vector_type(4)));
+        using lds_i16x4 = __attribute__((address_space(3))) i16x4;
+        const char *base = tile + 16 * t * RB;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + (v0 ^ (uint32_t)(db << 6))));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + (v1 ^ (uint32_t)(db << 6))));
+        return __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
     // Global byte offset (within a tile) that lane `lane` loads in DMA piece J:
     // rows J * 1024 / RB .., physical chunk lane % NC, logical chunk
     // (lane % NC) ^ swz(row).
@@ -447,6 +463,11 @@ __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0f70);
 // After the barrier that publishes DMA-filled LDS: the compiler does not see
 // the DMA as a store to the LDS arrays, so make it assume LDS has changed.
 __device__ __forceinline__ void lds_changed() { __asm__ volatile("" ::: "memory"); }
+
+// Hides a register's value from the optimiser (no instruction is emitted), so
+// that values derived from it inside a loop are not hoisted out of the loop
+// and kept live across it.
+__device__ __forceinline__ void opaque(uint32_t &x) { __asm__ volatile("" : "+v"(x)); }
 
 // Block height that gives each of NT threads one staging block of an R x D
 // tile when possible (4 rows at most).
