@@ -263,9 +263,9 @@ __device__ __forceinline__ void uniform_switch(int v, F &&f) {
 // of 32 x KS key slices (the map's ceil(h*w / 32) blocks of 32 keys split
 // evenly; a ragged last block is masked). Wave w runs on SIMD w % 4, so the
 // KS slices of one query sub-block share a SIMD. The head's whole K^T and
-// V^T (zero past h*w) and the Q^T block are fetched in one burst of loads;
-// Q^T and K^T are written to LDS first and the score products start while
-// V^T is still arriving;
+// V^T (zero past h*w) and the Q^T block are fetched with 16-byte loads:
+// Q^T and K^T first, written to LDS, then V^T, whose loads are issued once
+// Q^T and K^T have landed and arrive while the score products run;
 // each wave keeps the scores of its key slice in registers, so its softmax
 // needs one exact row max and one exp2 pass, no online rescaling; its block
 // loops have wave-uniform trip counts. The KS slices of a query sub-block
@@ -374,9 +374,6 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, KS
     for (int i = 0; i < K_PER; ++i)
         if (KD % RPP == 0 || rbase + RPP * i < KD) rk[i] = load_vec(KD + rbase + RPP * i, pk);
 #pragma unroll
-    for (int i = 0; i < V_PER; ++i)
-        if (DV % RPP == 0 || rbase + RPP * i < DV) rv[i] = load_vec(2 * KD + rbase + RPP * i, pk);
-#pragma unroll
     for (int i = 0; i < Q_PER; ++i)
         if (KD % QRP == 0 || qr + QRP * i < KD) *reinterpret_cast<uint4 *>(Qt + (qr + QRP * i) * LDQ + qc) = rq[i];
 #pragma unroll
@@ -384,6 +381,12 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, KS
         if (KD % RPP == 0 || rbase + RPP * i < KD)
             *reinterpret_cast<uint4 *>(Kt + (rbase + RPP * i) * LDKT + pk) = rk[i];
     __syncthreads();
+    // V^T (two thirds of the bytes) is requested only now, so that Q^T and
+    // K^T, which the score products need first, do not share the memory
+    // system with it; it streams in during those products
+#pragma unroll
+    for (int i = 0; i < V_PER; ++i)
+        if (DV % RPP == 0 || rbase + RPP * i < DV) rv[i] = load_vec(2 * KD + rbase + RPP * i, pk);
 
     // this wave: queries q0 + 32 qs + [0, 32), key blocks kb0 + [0, nb): the
     // map's ceil(hw / 32) key blocks split evenly over the KS slices (the
@@ -426,9 +429,8 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, KS
         }
         m = xhalf_max(mx) * scale_log2;  // exact max of this slice, log2 units
     }
-    // V^T (two thirds of the loaded bytes) goes to LDS only now: its loads
-    // were issued with those of Q and K, and stream in during the products
-    // above
+    // V^T goes to LDS only now: its loads were issued after Q^T and K^T had
+    // landed and streamed in during the products above
 #pragma unroll
     for (int i = 0; i < V_PER; ++i) {
         if (DV % RPP == 0 || rbase + RPP * i < DV) {  // V^T rows are 8-byte aligned
