@@ -175,7 +175,8 @@ __device__ __forceinline__ void fwd_tile(const typename Traits<DT>::elem *kt, co
 
 // One 64-key tile of the 16-bit forward on DMA-filled swizzled tiles (see
 // SwzTile): the same steps as fwd_tile, with fragment addresses precomputed
-// per lane.
+// per lane; the fast pass's steady tile (no mask, no max) has its own
+// phase-ordered schedule.
 template <Dt DT, int D, bool MASK, bool FAST, bool FIRST>
 __device__ __forceinline__ void fwd_tile_dma(const char *kt, const char *vt, const SwzTile<DT, D> &sw,
                                              const typename Traits<DT>::frag (&qf)[D / 16], f32x16 (&acc)[D / 32],
@@ -185,6 +186,55 @@ __device__ __forceinline__ void fwd_tile_dma(const char *kt, const char *vt, con
     constexpr int NKB = 2, NDB = D / 32, TS = D / 16, TP = 2;
     const int h = lane >> 5;
     f32x16 s[NKB];
+    if constexpr (FAST && !FIRST && !MASK) {
+        // The steady tile of the fast pass in three phases of one kind each,
+        // their order pinned by scheduling barriers: the score products back
+        // to back with each K fragment read two products ahead; the softmax
+        // as VALU work only; the P V products back to back with each V^T
+        // fragment read two products ahead (the first two before the
+        // softmax). VALU work between a wave's own products slows its matrix
+        // stream, while the other wave of the SIMD fills the softmax phase
+        // with its products (4% fewer cycles at N 4096, D 128 than the
+        // compiler's interleaved schedule).
+        constexpr int AK = 2, AV = 2, NP = NKB * TP * NDB;
+        frag kq[NKB * TS], vq[NP];
+        auto read_k = [&](int j) { kq[j] = sw.k(kt, j / TS, j % TS); };
+        auto read_v = [&](int i) { vq[i] = sw.vt(vt, i / (TP * NDB), (i / NDB) % TP, i % NDB); };
+#pragma unroll
+        for (int j = 0; j < AK; ++j) read_k(j);
+        s[0] = zero16();
+        s[1] = zero16();
+#pragma unroll
+        for (int j = 0; j < NKB * TS; ++j) {
+            if (j + AK < NKB * TS) read_k(j + AK);
+            __builtin_amdgcn_sched_barrier(0);
+            s[j / TS] = Tr::mfma(kq[j], qf[j % TS], s[j / TS]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < AV; ++i) read_v(i);
+        __builtin_amdgcn_sched_barrier(0);
+        const float neg_m = -m_ref;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int c = 0; c < 16; ++c) s[kb][c] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][c], scale_log2, neg_m));
+        l_run += sum16(s[0]) + sum16(s[1]);
+        frag pf[NKB][TP];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int t = 0; t < TP; ++t) pf[kb][t] = c_to_frag<DT>(s[kb], t);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            if (i + AV < NP) read_v(i + AV);
+            __builtin_amdgcn_sched_barrier(0);
+            acc[i % NDB] = Tr::mfma(vq[i], pf[i / (TP * NDB)][(i / NDB) % TP], acc[i % NDB]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        return;
+    }
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
         s[kb] = zero16();
