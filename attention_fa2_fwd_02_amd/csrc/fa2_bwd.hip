@@ -187,26 +187,64 @@ __device__ __forceinline__ void dq_pass_dma(__amdgpu_buffer_rsrc_t krs, __amdgpu
             }
         }
     };
+    // One 64-key tile, per 32-key block kb in phases of one kind each, their
+    // order pinned by scheduling barriers: the S products, the dP products,
+    // the softmax and dS as VALU work only, the dQ products. Every LDS
+    // operand is read two products ahead, the next block's first ones
+    // during the current block's last products, from the precomputed
+    // per-lane offsets. VALU work between a wave's own products (an
+    // interleaved exponential, or an address XOR) slows its matrix stream;
+    // the other wave of the SIMD fills the softmax phase (12% fewer cycles
+    // at N 4096, D 128 than the compiler's interleaved schedule).
     auto tile_fn = [&](const char *kt, const char *vt) {
+        constexpr int AHEAD = 2;
+        constexpr int OPK = 2 * TS + 2 * NDB, NOP = 2 * OPK;  // operands per key block / per tile
+        frag op[NOP];
+        // operand j: key block j / OPK; then K (S), V (dP), transposed K (dQ)
+        auto read = [&](int j) {
+            const int kb = j / OPK, r = j % OPK;
+            if (r < TS)
+                op[j] = sw.k(kt, kb, r);
+            else if (r < 2 * TS)
+                op[j] = sw.k(vt, kb, r - TS);
+            else
+                op[j] = sw.vt(kt, kb, (r - 2 * TS) / NDB, (r - 2 * TS) % NDB);
+        };
+#pragma unroll
+        for (int j = 0; j < AHEAD; ++j) read(j);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            // the S chain first, so that its exponentials can be scheduled
-            // among the dP products
+            const int base = kb * OPK;
             f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-            for (int t = 0; t < TS; ++t) s = Tr::mfma(sw.k(kt, kb, t), qf[t], s);
+            for (int t = 0; t < TS; ++t) {
+                if (base + t + AHEAD < NOP) read(base + t + AHEAD);
+                __builtin_amdgcn_sched_barrier(0);
+                s = Tr::mfma(op[base + t], qf[t], s);
+                __builtin_amdgcn_sched_barrier(0);
+            }
 #pragma unroll
-            for (int t = 0; t < TS; ++t) dp = Tr::mfma(sw.k(vt, kb, t), df[t], dp);
+            for (int t = 0; t < TS; ++t) {
+                const int j = base + TS + t;
+                if (j + AHEAD < NOP) read(j + AHEAD);
+                __builtin_amdgcn_sched_barrier(0);
+                dp = Tr::mfma(op[j], df[t], dp);
+                __builtin_amdgcn_sched_barrier(0);
+            }
 #pragma unroll
             for (int c = 0; c < 16; ++c) {
                 const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c], scale_log2, -lse2));
                 s[c] = p * (dp[c] - dl);
             }
+            const frag dsf[2] = {c_to_frag<DT>(s, 0), c_to_frag<DT>(s, 1)};
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const frag dsf = c_to_frag<DT>(s, t);
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) acc[db] = Tr::mfma(sw.vt(kt, kb, t, db), dsf, acc[db]);
+            for (int i = 0; i < 2 * NDB; ++i) {
+                const int j = base + 2 * TS + i;
+                if (j + AHEAD < NOP) read(j + AHEAD);
+                __builtin_amdgcn_sched_barrier(0);
+                acc[i % NDB] = Tr::mfma(op[j], dsf[i / NDB], acc[i % NDB]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
