@@ -483,26 +483,31 @@ __device__ __forceinline__ void dkdv_pass_dma(__amdgpu_buffer_rsrc_t qrs, __amdg
 #pragma unroll
     for (int i = 0; i < NDB; ++i) accK[i] = accV[i] = zero16();
 
-    // One query tile. The operands come from LDS ahead of their products, in
-    // an order pinned by scheduling barriers: the Q, dO and V fragments of
-    // step t + 1 are read before the S and dP products of step t, and the
-    // transposed dO / Q fragment of dV / dK product i + 2 before product i
-    // (left to itself at 256 registers, the compiler reads each operand just
-    // before its product and waits for it, which left the matrix pipe idle
-    // about 40% of the time). The offsets are rebuilt from three base
-    // registers per tile to make room for the operands in flight.
+    // One query tile in phases of one kind each, their order pinned by
+    // scheduling barriers: the S and dP products, the softmax and dS as VALU
+    // work only, the dV and dK products. The operands come from LDS ahead of
+    // their products: the Q, dO and V fragments of step t + 1 before the S
+    // and dP products of step t, the transposed dO / Q fragment of dV / dK
+    // product i + 2 before product i (left to itself at 256 registers, the
+    // compiler read each operand just before its product and waited for it,
+    // which left the matrix pipe idle about 40% of the time). The S / dP
+    // reads use the precomputed per-lane offsets; the eight transposed-read
+    // offsets are rebuilt per tile from two base registers (the XOR of a
+    // constant) between the products and the softmax, which leaves room for
+    // the operands in flight and keeps address arithmetic out of the product
+    // phases (VALU work between a wave's own products slows its matrix
+    // stream).
     auto tile_fn = [&](const char *qt, const char *dt, const float *ls, const float *es) {
         constexpr int AHEAD1 = 1, AHEAD2 = 2;
-        uint32_t k0 = sw.koff[0], v0 = sw.voff[0][0], v1 = sw.voff[0][1];
-        opaque(k0);
+        uint32_t v0 = sw.voff[0][0], v1 = sw.voff[0][1];
         opaque(v0);
         opaque(v1);
         f32x16 s = zero16(), dp = zero16();
         frag qa[TS], da[TS], va[TS];
         auto read1 = [&](int t) {
-            qa[t] = Sw::k_at(qt, k0, t);
-            da[t] = Sw::k_at(dt, k0, t);
-            va[t] = Sw::k_at(vown, k0, t);
+            qa[t] = sw.k(qt, 0, t);
+            da[t] = sw.k(dt, 0, t);
+            va[t] = sw.k(vown, 0, t);
         };
 #pragma unroll
         for (int t = 0; t < AHEAD1; ++t) read1(t);
@@ -517,9 +522,15 @@ __device__ __forceinline__ void dkdv_pass_dma(__amdgpu_buffer_rsrc_t qrs, __amdg
         // A operands of the 4 NDB dV / dK products, i = 2 (NDB t + db) + (0: dV, 1: dK)
         constexpr int NP = 4 * NDB;
         frag ob[NP];
+        uint32_t vo[NDB][2];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            vo[db][0] = Sw::vt_off(v0, db);
+            vo[db][1] = Sw::vt_off(v1, db);
+        }
         auto read2 = [&](int i) {
             const int t = i / (2 * NDB), db = (i >> 1) % NDB;
-            ob[i] = Sw::vt_at((i & 1) ? qt : dt, v0, v1, t, db);
+            ob[i] = Sw::vt_pair((i & 1) ? qt : dt, vo[db][0], vo[db][1], t);
         };
 #pragma unroll
         for (int i = 0; i < AHEAD2; ++i) read2(i);

@@ -422,20 +422,18 @@ struct SwzTile {
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + voff[db][1]));
         return __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
-    // The same reads from the step-0 offsets alone: the chunk index of step t
-    // (or d block db) is that of step 0 XOR 2t (or 4 db), and the XOR only
-    // touches the chunk bits of the offset. A caller that passes koff[0] /
-    // voff[0][*] through opaque() once per tile keeps one register per base
-    // instead of TS + 2 NDB loop-invariant offsets.
-    __device__ static __forceinline__ frag k_at(const char *tile, uint32_t k0, int t) {
-        return *reinterpret_cast<const frag *>(tile + (k0 ^ (uint32_t)(t << 5)));
-    }
-    __device__ static __forceinline__ frag vt_at(const char *tile, uint32_t v0, uint32_t v1, int t, int db) {
+    // voff[db][hi] from voff[0][hi]: the chunk index of d block db is that of
+    // block 0 XOR 4 db, and the XOR only touches the chunk bits of the
+    // offset, so a caller can keep two base registers (passed through
+    // opaque() once per tile) instead of 2 NDB loop-invariant offsets.
+    __device__ static __forceinline__ uint32_t vt_off(uint32_t v0, int db) { return v0 ^ (uint32_t)(db << 6); }
+    // vt() with the pair of offsets given: kb = 0, keys 16 t ..
+    __device__ static __forceinline__ frag vt_pair(const char *tile, uint32_t lo_off, uint32_t hi_off, int t) {
         typedef short i16x4 __attribute__((ext_vector_type(4)));
         using lds_i16x4 = __attribute__((address_space(3))) i16x4;
         const char *base = tile + 16 * t * RB;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + (v0 ^ (uint32_t)(db << 6))));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + (v1 ^ (uint32_t)(db << 6))));
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + lo_off));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + hi_off));
         return __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
     // Global byte offset (within a tile) that lane `lane` loads in DMA piece J:
