@@ -602,7 +602,13 @@ __device__ __forceinline__ void dkdv_pass_dma(__amdgpu_buffer_rsrc_t qrs, __amdg
     // `col` holds dK / dV of key col, d = 32 db + 8 g + 4 h + 0..3; it writes
     // those 8 bytes at the swizzled place of row col, then the wave reads
     // back whole 16-byte chunks, 16 lanes per 256-byte row, and stores them.
-    const int col = lane & 31;
+    // Its lane-derived offsets are computed from a copy of the lane index
+    // the optimiser cannot match with the prologue's (it would otherwise keep
+    // the prologue's across the loop in spilled registers: 44 bytes per lane
+    // stored and reloaded once per wave, 16% more HBM writes than dK + dV).
+    uint32_t lane_e = (uint32_t)lane;
+    opaque(lane_e);
+    const int col = lane_e & 31, he = lane_e >> 5;
     auto emit = [&](const f32x16 (&acc)[NDB], float mul, elem *rows) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -612,12 +618,12 @@ __device__ __forceinline__ void dkdv_pass_dma(__amdgpu_buffer_rsrc_t qrs, __amdg
 #pragma unroll
                 for (int i = 0; i < 4; ++i) v[i] = static_cast<elem>(acc[db][4 * g + i] * mul);
                 const int c = 4 * db + g;  // logical chunk of d = 32 db + 8 g
-                *reinterpret_cast<typename Tr::half_frag *>(vown + col * RB + ((c ^ swz<D>(col)) << 4) + 8 * h) = v;
+                *reinterpret_cast<typename Tr::half_frag *>(vown + col * RB + ((c ^ swz<D>(col)) << 4) + 8 * he) = v;
             }
         constexpr int PER = 32 * NC / 64;  // chunks per lane
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int idx = lane + 64 * i, r = idx / NC, p = idx % NC;
+            const int idx = (int)lane_e + 64 * i, r = idx / NC, p = idx % NC;
             const uint4 w = *reinterpret_cast<const uint4 *>(vown + r * RB + (p << 4));
             const int c = p ^ swz<D>(r);
             if (krow0 + 32 * wv + r < n_k)
