@@ -159,6 +159,33 @@ def test_fwd_many_blocks_and_rerun(dt, mult):
     _err("LSE", _np(lse), lse_ref, tol, case)
 
 
+@pytest.mark.parametrize("dt,mult,nk", [("f16", 6.0, 256), ("bf16", 16.0, 256), ("bf16", 1.0, 1280),
+                                        ("f16", 1.0, 512), ("bf16", 16.0, 1280)])
+def test_fwd_persistent_many_blocks_and_rerun(dt, mult, nk):
+    """The persistent forward (head_dim 128, 16-bit, key length a multiple of
+    256, at least 512 query blocks of 256 rows): 264 heads x 2 query blocks
+    (the second ragged, 44 rows) = 528 blocks over 256 workgroups, so the
+    blocks per workgroup differ; 256 keys (the block's first tile and its
+    last three steps only) or 1280 (the four-tile loop as well). With
+    mult > 1, every 7th head has its last 64 keys equal to mult x its query
+    0, far above the first tile's max: those blocks redo their rows with the
+    exact pass and the block after each starts from scratch. Every output
+    against the oracle."""
+    bh, nq, d = 264, 300, 128
+    case = f"persistent fwd {dt} x{mult} nk={nk}"
+    print(case, flush=True)
+    x = _inputs(dt, bh, nq, nk, d, seed=91 + nk)
+    k = x["k"].clone()
+    if mult != 1.0:
+        k[::7, nk - 64:, :] = (mult * x["q"][::7, :1, :].float()).to(k.dtype)
+    o, lse = fa2.fa2_fwd(x["q"], k, x["v"])
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_fwd(x["q"], k, x["v"], 1 / math.sqrt(d))
+    tol = TOL[DTYPES[dt]]
+    _err("O", _np(o), o_ref, tol, case)
+    _err("LSE", _np(lse), lse_ref, tol, case)
+
+
 def test_fwd_c1_tiny_f32():
     w = workloads.C1
     x = workloads.attn_inputs(w, device=DEV)
