@@ -125,7 +125,7 @@ def _flush_buffer(torch):
 # kernels of the step (rocprofv3 kernel names, template arguments as printed)
 # and the sources their code comes from
 TRAFFIC_KERNELS = {
-    "fwd": ("fwd_kernel<(fa2mi::Dt)2, 128, 64, 8, false>", ["attention_fa2_fwd_02_amd/csrc/fa2_fwd.hip"]),
+    "fwd": ("fwd_stream_kernel<(fa2mi::Dt)2, 128>", ["attention_fa2_fwd_02_amd/csrc/fa2_fwd.hip"]),
     "dkdv": ("dkdv_kernel<(fa2mi::Dt)2, 128, 32, 8>", ["attention_fa2_fwd_02_amd/csrc/fa2_bwd.hip"]),
     "dq": ("dq_kernel<(fa2mi::Dt)2, 128, 64, 8>", ["attention_fa2_fwd_02_amd/csrc/fa2_bwd.hip"]),
     "delta": ("delta_kernel<(fa2mi::Dt)2, 128>", ["attention_fa2_fwd_02_amd/csrc/fa2_bwd.hip"]),
