@@ -8,6 +8,8 @@
 //   delta_kernel - delta_i = rowsum(O * dO) (fp32), read by both others;
 //   dq_kernel    - one workgroup per 32*WAVES query rows, looping over key
 //                  tiles (the forward's structure with dS in place of P);
+//                  dq_stream_kernel, its persistent form at head_dim 128,
+//                  walks query blocks with one workgroup per CU;
 //   dkdv_kernel  - one workgroup per 32*WAVES key rows, looping over query
 //                  tiles; K and V of the wave's 32 keys stay in registers.
 #include <type_traits>
@@ -405,6 +407,268 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) store4_b<DT>(op + 32 * db + 8 * g + 4 * h, acc[db], g, scale);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Persistent form of the 8-wave 16-bit dQ at head_dim 128 (as the forward's
+// fwd_stream_kernel), for key lengths that are a multiple of 256 with at
+// least two 256-row query blocks per CU: one workgroup per CU walks query
+// blocks i * gridDim.x + (g % 8) * gridDim.x / 8 + g / 8, so a block's start
+// and end overlap the neighbouring blocks' tiles. Four LDS stages (tile t of
+// every block in stage t % 4, fetched two ahead, one barrier per tile); a
+// block's last two steps fetch the next block's tiles 0 and 1, and the next
+// block's Q, dO, lse and delta are loaded into their registers during the
+// last tile, each right after its last use (Q after the second key block's
+// score products, dO after its dP products, lse and delta after its dS).
+// K stages sit in the low 64 KiB and V stages above; V is read with row
+// offsets that carry the 64 KiB as a bias, so every LDS read folds its
+// constant into the 16-bit offset field.
+struct NoHook {
+    __device__ __forceinline__ void operator()() const {}
+};
+
+// One 64-key tile of dQ (as dq_pass_dma's tile): swk reads K (rows and
+// transposed), swv the V rows of a tile addressed vt - bias. Hooks run after
+// the second key block's S products (hq), dP products (hd) and dS (hl).
+template <Dt DT, int D, class HQ, class HD, class HL>
+__device__ __forceinline__ void dq_tile_stream(const char *kt, const char *vt, const SwzTile<DT, D> &swk,
+                                               const SwzTile<DT, D> &swv,
+                                               const typename Traits<DT>::frag (&qf)[D / 16],
+                                               const typename Traits<DT>::frag (&df)[D / 16], float lse2, float dl,
+                                               f32x16 (&acc)[D / 32], float scale_log2, const HQ &hq, const HD &hd,
+                                               const HL &hl) {
+    using Tr = Traits<DT>;
+    using frag = typename Tr::frag;
+    constexpr int NDB = D / 32, TS = D / 16, AHEAD = 2;
+    constexpr int OPK = 2 * TS + 2 * NDB, NOP = 2 * OPK;  // operands per key block / per tile
+    frag op[NOP];
+    // operand j: key block j / OPK; then K (S), V (dP), transposed K (dQ)
+    auto read = [&](int j) {
+        const int kb = j / OPK, r = j % OPK;
+        if (r < TS)
+            op[j] = swk.k(kt, kb, r);
+        else if (r < 2 * TS)
+            op[j] = swv.k(vt, kb, r - TS);
+        else
+            op[j] = swk.vt(kt, kb, (r - 2 * TS) / NDB, (r - 2 * TS) % NDB);
+    };
+#pragma unroll
+    for (int j = 0; j < AHEAD; ++j) read(j);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        const int base = kb * OPK;
+        f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+        for (int t = 0; t < TS; ++t) {
+            if (base + t + AHEAD < NOP) read(base + t + AHEAD);
+            __builtin_amdgcn_sched_barrier(0);
+            s = Tr::mfma(op[base + t], qf[t], s);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (kb == 1) {
+            hq();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int t = 0; t < TS; ++t) {
+            const int j = base + TS + t;
+            if (j + AHEAD < NOP) read(j + AHEAD);
+            __builtin_amdgcn_sched_barrier(0);
+            dp = Tr::mfma(op[j], df[t], dp);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (kb == 1) {
+            hd();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c], scale_log2, -lse2));
+            s[c] = p * (dp[c] - dl);
+        }
+        const frag dsf[2] = {c_to_frag<DT>(s, 0), c_to_frag<DT>(s, 1)};
+        if (kb == 1) hl();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 2 * NDB; ++i) {
+            const int j = base + 2 * TS + i;
+            if (j + AHEAD < NOP) read(j + AHEAD);
+            __builtin_amdgcn_sched_barrier(0);
+            acc[i % NDB] = Tr::mfma(op[j], dsf[i / NDB], acc[i % NDB]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+constexpr int kDqStreamGrid = 256;  // one workgroup per CU
+
+template <Dt DT, int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_stream_kernel(
+    const typename Traits<DT>::elem *__restrict__ Q, const typename Traits<DT>::elem *__restrict__ K,
+    const typename Traits<DT>::elem *__restrict__ V, const typename Traits<DT>::elem *__restrict__ dO,
+    const float *__restrict__ LSE, const float *__restrict__ Delta, typename Traits<DT>::elem *__restrict__ dQ,
+    int n_q, int n_k, int n_qblocks, int total_blocks, float scale_log2, float scale) {
+    using Tr = Traits<DT>;
+    using elem = typename Tr::elem;
+    using frag = typename Tr::frag;
+    using Sw = SwzTile<DT, D>;
+    constexpr int WAVES = 8, BR = 32 * WAVES, BC = Sw::ROWS, NDB = D / 32, TS = D / 16;
+    constexpr int BYTES = Sw::BYTES, PIECES = Sw::PIECES;
+    constexpr int NPW = 2 * (PIECES / WAVES);  // DMA instructions per wave and tile
+    constexpr int NQ = 2 * TS + 2;             // loads of a block's Q, dO, lse and delta per lane
+    static_assert(PIECES % WAVES == 0 && NPW + NQ < 64 && NPW < 16, "pieces per wave");
+    __shared__ __attribute__((aligned(1024))) char K0[BYTES];
+    __shared__ __attribute__((aligned(1024))) char K1[BYTES];
+    __shared__ __attribute__((aligned(1024))) char K2[BYTES];
+    __shared__ __attribute__((aligned(1024))) char K3[BYTES];
+    __shared__ __attribute__((aligned(1024))) char V0[BYTES];
+    __shared__ __attribute__((aligned(1024))) char V1[BYTES];
+    __shared__ __attribute__((aligned(1024))) char V2[BYTES];
+    __shared__ __attribute__((aligned(1024))) char V3[BYTES];
+    constexpr uint32_t kVBias = 4 * BYTES;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int h = lane >> 5, col = lane & 31;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    Sw swk;
+    swk.init(lane);
+    Sw swv = swk;
+#pragma unroll
+    for (int t = 0; t < TS; ++t) {
+        swv.koff[t] += kVBias;
+        opaque(swv.koff[t]);
+    }
+    const int ntiles = n_k / BC;
+    const int G = gridDim.x;
+    int L = (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8);
+    if (L >= total_blocks) return;
+
+    const uint32_t kv_bytes = (uint32_t)n_k * D * (uint32_t)sizeof(elem);
+    auto k_rsrc = [&](int blk) { return make_rsrc(K + (int64_t)(blk / n_qblocks) * n_k * D, kv_bytes); };
+    auto v_rsrc = [&](int blk) { return make_rsrc(V + (int64_t)(blk / n_qblocks) * n_k * D, kv_bytes); };
+    // rows of block blk (rows at or past n_q read as zero)
+    auto row_rsrc = [&](const void *base, int blk, int row_bytes) {
+        const int bh = blk / n_qblocks, q0 = (blk % n_qblocks) * BR;
+        return make_rsrc(static_cast<const char *>(base) + ((int64_t)bh * n_q + q0) * row_bytes,
+                         (uint32_t)min(BR, n_q - q0) * (uint32_t)row_bytes);
+    };
+    constexpr int RB = D * (int)sizeof(elem);
+    // this lane's fragment t: row wave * 32 + col, columns 16 t + 8 h ..
+    const uint32_t q_lane = (uint32_t)((wave * 32 + col) * RB + h * Tr::KPL * (int)sizeof(elem));
+    const uint32_t l_lane = (uint32_t)((wave * 32 + col) * 4);
+    frag qf[TS], df[TS];
+    float lse_raw, dl;
+    auto load_q = [&](__amdgpu_buffer_rsrc_t r) {
+#pragma unroll
+        for (int t = 0; t < TS; ++t) qf[t] = __builtin_bit_cast(frag, buffer_load16(r, q_lane + 32 * t));
+    };
+    auto load_do = [&](__amdgpu_buffer_rsrc_t r) {
+#pragma unroll
+        for (int t = 0; t < TS; ++t) df[t] = __builtin_bit_cast(frag, buffer_load16(r, q_lane + 32 * t));
+    };
+    auto load_ld = [&](__amdgpu_buffer_rsrc_t lr, __amdgpu_buffer_rsrc_t er) {
+        lse_raw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lr, l_lane, 0, 0));
+        dl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(er, l_lane, 0, 0));
+    };
+    // this wave's DMA pieces of tile `tile` (piece J to wave J % WAVES)
+    auto dma_tile = [&](__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, int tile, char *kd, char *vd) {
+        const uint32_t t0 = (uint32_t)tile * (uint32_t)BYTES;
+#pragma unroll
+        for (int j = 0; j < PIECES / WAVES; ++j) {
+            const int J = wv + WAVES * j;
+            const uint32_t off = t0 + Sw::piece_off(J, lane);
+            dma16(kr, off, kd + 1024 * J);
+            dma16(vr, off, vd + 1024 * J);
+        }
+    };
+
+    __amdgpu_buffer_rsrc_t krs = k_rsrc(L), vrs = v_rsrc(L);
+    load_q(row_rsrc(Q, L, RB));
+    load_do(row_rsrc(dO, L, RB));
+    load_ld(row_rsrc(LSE, L, 4), row_rsrc(Delta, L, 4));
+    dma_tile(krs, vrs, 0, K0, V0);
+    dma_tile(krs, vrs, 1, K1, V1);
+    // Q, dO, lse, delta and tile 0 landed (loads complete in order)
+    __builtin_amdgcn_s_waitcnt(0x0f70 | NPW);
+    lds_changed();
+    __builtin_amdgcn_s_barrier();
+    lds_changed();
+
+    f32x16 acc[NDB];
+    for (;;) {
+        const int Ln = L + G;
+        const bool has_next = Ln < total_blocks;
+        // past the last block the look-ahead reads zeros: tiles past this
+        // head's end, and rows of an empty range
+        const __amdgpu_buffer_rsrc_t nkrs = has_next ? k_rsrc(Ln) : krs;
+        const __amdgpu_buffer_rsrc_t nvrs = has_next ? v_rsrc(Ln) : vrs;
+        const int ntile0 = has_next ? 0 : ntiles;
+        const int qrow = (L % n_qblocks) * BR + wave * 32 + col;
+        // rows past n_q: lse = +inf, so every P is 0 (their Q and dO are zero)
+        const float lse2 = qrow < n_q ? lse_raw * kLog2e : INFINITY;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) acc[d] = zero16();
+        // step t: DMA of tile t + 2 (of this block, or tile t + 2 - ntiles of
+        // the next) into stage (t + 2) % 4, last read in step t - 2; tile t;
+        // wait for tile t + 1's pieces (WAITN: the loads issued after them,
+        // tile t + 2's and, in the last step, the next block's rows); barrier
+        auto step = [&](auto stage_tag, auto waitn_tag, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                        int dtile, const auto &hq, const auto &hd, const auto &hl) {
+            constexpr int S = decltype(stage_tag)::value;
+            constexpr int WAITN = decltype(waitn_tag)::value;
+            char *const kc = S == 0 ? K0 : S == 1 ? K1 : S == 2 ? K2 : K3;
+            char *const vc = S == 0 ? V0 : S == 1 ? V1 : S == 2 ? V2 : V3;
+            char *const kn = S == 0 ? K2 : S == 1 ? K3 : S == 2 ? K0 : K1;
+            char *const vn = S == 0 ? V2 : S == 1 ? V3 : S == 2 ? V0 : V1;
+            dma_tile(kr, vr, dtile, kn, vn);
+            __builtin_amdgcn_sched_barrier(0);
+            dq_tile_stream<DT, D>(kc, vc - kVBias, swk, swv, qf, df, lse2, dl, acc, scale_log2, hq, hd, hl);
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(0x0f70 | (WAITN & 15) | ((WAITN >> 4) << 14));
+            lds_changed();
+            __builtin_amdgcn_s_barrier();
+            lds_changed();
+        };
+        using C0 = std::integral_constant<int, 0>;
+        using C1 = std::integral_constant<int, 1>;
+        using C2 = std::integral_constant<int, 2>;
+        using C3 = std::integral_constant<int, 3>;
+        using WN = std::integral_constant<int, NPW>;
+        using WQ = std::integral_constant<int, NPW + NQ>;
+        const NoHook none;
+        int t = 0;
+        for (; t + 8 <= ntiles; t += 4) {
+            step(C0{}, WN{}, krs, vrs, t + 2, none, none, none);
+            step(C1{}, WN{}, krs, vrs, t + 3, none, none, none);
+            step(C2{}, WN{}, krs, vrs, t + 4, none, none, none);
+            step(C3{}, WN{}, krs, vrs, t + 5, none, none, none);
+        }
+        const __amdgpu_buffer_rsrc_t nq = has_next ? row_rsrc(Q, Ln, RB) : make_rsrc(Q, 0);
+        const __amdgpu_buffer_rsrc_t nd = has_next ? row_rsrc(dO, Ln, RB) : make_rsrc(dO, 0);
+        const __amdgpu_buffer_rsrc_t nl = has_next ? row_rsrc(LSE, Ln, 4) : make_rsrc(LSE, 0);
+        const __amdgpu_buffer_rsrc_t ne = has_next ? row_rsrc(Delta, Ln, 4) : make_rsrc(Delta, 0);
+        step(C0{}, WN{}, krs, vrs, ntiles - 2, none, none, none);
+        step(C1{}, WN{}, krs, vrs, ntiles - 1, none, none, none);
+        step(C2{}, WN{}, nkrs, nvrs, ntile0, none, none, none);
+        step(C3{}, WQ{}, nkrs, nvrs, ntile0 + 1, [&]() { load_q(nq); }, [&]() { load_do(nd); },
+             [&]() { load_ld(nl, ne); });
+
+        // the next block's rows and tile 1 landed (issued during the last
+        // tile): waiting here, before the stores, keeps the next block's
+        // first products from waiting on the stores as well
+        wait_dma();
+        if (qrow < n_q) {
+            elem *op = dQ + ((int64_t)(L / n_qblocks) * n_q + qrow) * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) store4_b<DT>(op + 32 * db + 8 * g + 4 * h, acc[db], g, scale);
+        }
+        if (!has_next) break;
+        L = Ln;
+        krs = nkrs;
+        vrs = nvrs;
     }
 }
 
@@ -843,9 +1107,28 @@ static hipError_t dq_launch(const void *q, const void *k, const void *v, const v
 }
 
 template <Dt DT, int D>
+static hipError_t dq_stream_launch(const void *q, const void *k, const void *v, const void *d_o, const float *lse,
+                                   const float *delta, void *dq, const AttnShape &s, hipStream_t stream) {
+    using elem = typename Traits<DT>::elem;
+    const int nqb = (s.n_q + 255) / 256;
+    const int total = (int)(s.bh * nqb);
+    const float scale_log2 = (float)((double)s.scale * 1.4426950408889634);
+    hipLaunchKernelGGL((dq_stream_kernel<DT, D>), dim3(kDqStreamGrid), dim3(512), 0, stream, (const elem *)q,
+                       (const elem *)k, (const elem *)v, (const elem *)d_o, lse, delta, (elem *)dq, s.n_q, s.n_k,
+                       nqb, total, scale_log2, s.scale);
+    return hipGetLastError();
+}
+
+template <Dt DT, int D>
 static hipError_t dq_dispatch(const void *q, const void *k, const void *v, const void *d_o, const float *lse,
                               const float *delta, void *dq, const AttnShape &s, hipStream_t stream) {
     constexpr int64_t kCus = 256;
+    if constexpr (D == 128 && DT != Dt::F32) {
+        // key lengths in whole groups of four tiles and at least two query
+        // blocks per CU: the persistent launch
+        if (s.n_k >= 256 && s.n_k % 256 == 0 && s.bh * ((s.n_q + 255) / 256) >= 2 * kDqStreamGrid)
+            return dq_stream_launch<DT, D>(q, k, v, d_o, lse, delta, dq, s, stream);
+    }
     if (s.bh * ((s.n_q + 255) / 256) >= 2 * kCus) return dq_launch<DT, D, 8>(q, k, v, d_o, lse, delta, dq, s, stream);
     if (s.bh * ((s.n_q + 127) / 128) >= kCus) return dq_launch<DT, D, 4>(q, k, v, d_o, lse, delta, dq, s, stream);
     return dq_launch<DT, D, 2>(q, k, v, d_o, lse, delta, dq, s, stream);

@@ -127,7 +127,7 @@ def _flush_buffer(torch):
 TRAFFIC_KERNELS = {
     "fwd": ("fwd_stream_kernel<(fa2mi::Dt)2, 128>", ["attention_fa2_fwd_02_amd/csrc/fa2_fwd.hip"]),
     "dkdv": ("dkdv_kernel<(fa2mi::Dt)2, 128, 32, 8>", ["attention_fa2_fwd_02_amd/csrc/fa2_bwd.hip"]),
-    "dq": ("dq_kernel<(fa2mi::Dt)2, 128, 64, 8>", ["attention_fa2_fwd_02_amd/csrc/fa2_bwd.hip"]),
+    "dq": ("dq_stream_kernel<(fa2mi::Dt)2, 128>", ["attention_fa2_fwd_02_amd/csrc/fa2_bwd.hip"]),
     "delta": ("delta_kernel<(fa2mi::Dt)2, 128>", ["attention_fa2_fwd_02_amd/csrc/fa2_bwd.hip"]),
 }
 

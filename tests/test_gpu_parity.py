@@ -538,6 +538,28 @@ def test_bwd_workgroup_sizes(dt, d, shape):
         _err(name, _np(got), want, tol, case)
 
 
+@pytest.mark.parametrize("dt,nk", [("bf16", 256), ("f16", 1280), ("bf16", 1280)])
+def test_bwd_persistent_dq(dt, nk):
+    """The persistent dQ (head_dim 128, 16-bit, key length a multiple of
+    256, at least 512 query blocks of 256 rows): 264 heads x 2 query blocks
+    (the second ragged, 44 rows) = 528 blocks over 256 workgroups, so the
+    blocks per workgroup differ and the next block's rows, loaded during the
+    last tile, come from another head or past the last block; 256 keys (the
+    last four-step group only) or 1280 (the four-step loop as well). Every
+    dQ, dK and dV element against the oracle."""
+    bh, nq, d = 264, 300, 128
+    case = f"persistent dq {dt} nk={nk}"
+    print(case, flush=True)
+    x = _inputs(dt, bh, nq, nk, d, seed=700 + nk, with_do=True)
+    o, lse = fa2.fa2_fwd(x["q"], x["k"], x["v"])
+    dq, dk, dv = fa2.attention_bwd(x["q"], x["k"], x["v"], o, x["do"], lse)
+    torch.cuda.synchronize()
+    ref = oracle.attention_bwd(x["q"], x["k"], x["v"], x["do"], 1 / math.sqrt(d))
+    tol = TOL[DTYPES[dt]]
+    for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        _err(name, _np(got), want, tol, case)
+
+
 def test_bwd_delta_matches_rowsum():
     x = _inputs("bf16", 3, 130, 10, 128, seed=12, with_do=True)
     o = x["v"].new_empty(0)
