@@ -55,7 +55,9 @@ def _parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    # ten untimed steps (~0.16 s): the chip's clock under this load settles
+    # only after about 0.15 s of work
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-legs", action="store_true", help="skip the other-shape legs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0, help="oracle sample heads (0: three per thread)")
@@ -322,10 +324,25 @@ def main():
     print(json.dumps(out))
 
 
-def _time_fn(torch, fn, reps, warm=3, flush=None):
-    for _ in range(warm):
+def _warm(torch, fn, warm_s=0.25, min_calls=3):
+    """Untimed calls until about warm_s seconds of them have run. Under a
+    sustained load the chip's clock settles only after about 0.15 s: the LLM
+    forward took 3.66, 3.56 and 3.52 ms (medians of ten synchronized calls)
+    in three consecutive rounds after three warm-up calls, and back-to-back
+    calls converge to the same 3.52 ms, so a few warm-up calls time a clock
+    that is still ramping."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < min_calls or time.perf_counter() - t0 < warm_s:
         fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+
+
+def _time_fn(torch, fn, reps, flush=None):
+    _warm(torch, fn)
     ts = []
     for _ in range(reps):
         if flush is not None:
@@ -340,12 +357,10 @@ def _time_fn(torch, fn, reps, warm=3, flush=None):
     return ts[len(ts) // 2]
 
 
-def _time_batch(torch, fn, calls, warm=3):
+def _time_batch(torch, fn, calls):
     """Average time per call of `calls` back-to-back calls between two events
     (launch latency overlapped, as in a stream of blocks)."""
-    for _ in range(warm):
-        fn()
-    torch.cuda.synchronize()
+    _warm(torch, fn)
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
     for _ in range(calls):
