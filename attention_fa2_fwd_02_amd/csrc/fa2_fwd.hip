@@ -19,6 +19,10 @@
 //      rescaled by 2^(m - m') as in the online-softmax recurrence).
 //   4. O^T += V^T P^T on MFMA, P fed from registers as the B operand.
 // Epilogue: O = O^T / l rounded to the element type; LSE = ln2 * (m + log2 l).
+// 16-bit inputs at head_dim 128 with key lengths in whole 256-key groups and
+// at least two 256-row query blocks per CU run the persistent form
+// (fwd_stream_kernel): one 8-wave workgroup per CU walks the query blocks,
+// its K/V ring and Q loads running on from one block into the next.
 #include <type_traits>
 
 #include "fa2_device.h"
