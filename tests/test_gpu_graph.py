@@ -59,8 +59,13 @@ def test_psa_attn_fused_graph_replay():
     _replay_and_check(g, [out, lse], expected, lambda: fa2.psa_attn_fused(qkv, w.num_heads, w.key_dim, other))
 
 
-def test_attention_fwd_bwd_graph_replay():
-    bh, n_q, n_k, d = 4, 300, 333, 64
+@pytest.mark.parametrize("bh,n_q,n_k,d", [(4, 300, 333, 64), (264, 300, 256, 128)],
+                         ids=["per-block", "persistent"])
+def test_attention_fwd_bwd_graph_replay(bh, n_q, n_k, d):
+    """The small shape runs one workgroup per query (or key) block; the
+    second (528 query blocks of 256 rows at head_dim 128, keys a multiple of
+    256) selects the persistent forward and dQ, whose workgroups walk blocks
+    and keep nothing between launches."""
     print(f"graph fa2_fwd + backward bf16 bh={bh} n_q={n_q} n_k={n_k} d={d}", flush=True)
     w = workloads.AttnWorkload("graph", bh, n_q, n_k, d, "bf16", 61)
     x = workloads.attn_inputs(w, device=DEV, with_do=True)
