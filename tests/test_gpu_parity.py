@@ -227,8 +227,11 @@ def test_fwd_canaries_untouched():
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
 
 
-def test_fwd_deterministic():
-    x = _inputs("bf16", 4, 300, 500, 128, seed=8)
+@pytest.mark.parametrize("shape", [(4, 300, 500), (264, 300, 512)], ids=["per-block", "persistent"])
+def test_fwd_deterministic(shape):
+    # the second shape selects the persistent forward (528 query blocks)
+    bh, nq, nk = shape
+    x = _inputs("bf16", bh, nq, nk, 128, seed=8)
     a = fa2.fa2_fwd(x["q"], x["k"], x["v"])
     b = fa2.fa2_fwd(x["q"], x["k"], x["v"])
     torch.cuda.synchronize()
@@ -591,8 +594,11 @@ def test_bwd_c5_sampled():
     assert (dv.float().sum(1) - x["do"].float().sum(1)).abs().max().item() < 5e-2
 
 
-def test_bwd_deterministic():
-    x = _inputs("bf16", 2, 300, 260, 128, seed=13, with_do=True)
+@pytest.mark.parametrize("shape", [(2, 300, 260), (264, 300, 512)], ids=["per-block", "persistent"])
+def test_bwd_deterministic(shape):
+    # the second shape selects the persistent dQ (528 query blocks)
+    bh, nq, nk = shape
+    x = _inputs("bf16", bh, nq, nk, 128, seed=13, with_do=True)
     o, lse = fa2.fa2_fwd(x["q"], x["k"], x["v"])
     a = fa2.attention_bwd(x["q"], x["k"], x["v"], o, x["do"], lse)
     b = fa2.attention_bwd(x["q"], x["k"], x["v"], o, x["do"], lse)
