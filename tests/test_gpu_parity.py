@@ -720,6 +720,10 @@ def test_bwd_long_keys():
                                          (32, 1, 1, 1, 1), (64, 3, 1, 16, 24), (32, 2, 2, 13, 11),
                                          # whole-head kernel capacity (448 / 256 pixels) and one past it
                                          (32, 1, 2, 16, 28), (32, 1, 1, 1, 449),
+                                         # whole-head kernel at 7 key blocks per head (256 < h*w <= 448):
+                                         # ragged last key block, 3 and 4 workgroups per head
+                                         (32, 3, 5, 12, 22), (32, 2, 3, 16, 20), (32, 4, 2, 14, 28),
+                                         (32, 1, 3, 8, 55),
                                          (64, 1, 2, 16, 16), (64, 1, 1, 1, 257),
                                          # tiled kernel with 16-byte vector access (h*w % 8 == 0)
                                          (32, 1, 1, 16, 32), (64, 1, 2, 16, 24),
