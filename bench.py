@@ -370,6 +370,26 @@ def _time_batch(torch, fn, calls):
     return s.elapsed_time(e) / calls
 
 
+def _time_stream(torch, fn, calls, reps=3):
+    """Kernel throughput of a long launch: median over `reps` batches of the
+    average time per call of `calls` back-to-back calls between two events.
+    The host queues each call while the previous one runs, as in the step; the
+    median single call between two events is reported next to it as
+    `single_call_ms`."""
+    _warm(torch, fn)
+    ts = []
+    for _ in range(reps):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(calls):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        ts.append(s.elapsed_time(e) / calls)
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
 def _time_graph(torch, fn, calls, reps=5):
     """Average time per call of `calls` calls captured in one HIP graph,
     median over `reps` replays (launch work done at capture, as in a
@@ -493,9 +513,12 @@ def _leg_c3(torch, fa2, workloads, dev, legs):
     x = workloads.attn_inputs(w3, device=dev)
     o = torch.empty_like(x["q"])
     lse = torch.empty((w3.bh, w3.n_q), dtype=torch.float32, device=dev)
-    ms = _time_fn(torch, lambda: fa2.fa2_fwd(x["q"], x["k"], x["v"], w3.scale, o, lse), 10)
+    fwd3 = lambda: fa2.fa2_fwd(x["q"], x["k"], x["v"], w3.scale, o, lse)
+    ms = _time_stream(torch, fwd3, 10)
+    ms_single = _time_fn(torch, fwd3, 5)
     tf = w3.fwd_flops() / (ms * 1e-3) / 1e12
-    legs["c3_fwd"] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    legs["c3_fwd"] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                      "single_call_ms": round(ms_single, 4)}
     # Context, not a result: the same launch on constant inputs (Q = K =
     # 0.25, V = 0.5). The kernel runs the same instructions in the same
     # number of cycles whatever the data; what changes is the clock the chip
@@ -503,7 +526,7 @@ def _leg_c3(torch, fa2, workloads, dev, legs):
     # ratio of the two times is that clock ratio.
     for t, val in ((x["q"], 0.25), (x["k"], 0.25), (x["v"], 0.5)):
         t.fill_(val)
-    ms_c = _time_fn(torch, lambda: fa2.fa2_fwd(x["q"], x["k"], x["v"], w3.scale, o, lse), 10)
+    ms_c = _time_stream(torch, fwd3, 10)
     tf_c = w3.fwd_flops() / (ms_c * 1e-3) / 1e12
     legs["c3_fwd"].update({"const_inputs_ms": round(ms_c, 4), "const_inputs_tflops": round(tf_c, 1),
                            "const_inputs_frac_bf16_peak": round(tf_c / PEAK_BF16_TFLOPS, 4),
@@ -518,10 +541,12 @@ def _leg_c4(torch, fa2, workloads, dev, legs):
     x = workloads.attn_inputs(w4, device=dev)
     o = torch.empty_like(x["q"])
     lse = torch.empty((w4.bh, w4.n_q), dtype=torch.float32, device=dev)
-    ms = _time_fn(torch, lambda: fa2.fa2_fwd(x["q"], x["k"], x["v"], w4.scale, o, lse), 10)
+    fwd4 = lambda: fa2.fa2_fwd(x["q"], x["k"], x["v"], w4.scale, o, lse)
+    ms = _time_stream(torch, fwd4, 10)
+    ms_single = _time_fn(torch, fwd4, 5)
     tf = w4.fwd_flops() / (ms * 1e-3) / 1e12
-    legs["c4"] = {"ms": round(ms, 4), "tflops": round(tf, 1),
-                            "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    legs["c4"] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                  "single_call_ms": round(ms_single, 4)}
     del x, o, lse
     torch.cuda.empty_cache()
     print(f"[bench] leg c4 {legs['c4']}", file=sys.stderr, flush=True)
@@ -539,10 +564,11 @@ def _leg_c5(torch, fa2, workloads, dev, legs):
         fa2.fa2_bwd_dkdv(x["q"], x["k"], x["v"], x["do"], lse, delta, w5.scale, dk, dv)
         fa2.fa2_bwd_dq(x["q"], x["k"], x["v"], x["do"], lse, delta, w5.scale, dq)
 
-    ms = _time_fn(torch, bwd, 10)
+    ms = _time_stream(torch, bwd, 10)
+    ms_single = _time_fn(torch, bwd, 5)
     tf = w5.bwd_flops() / (ms * 1e-3) / 1e12
-    legs["c5"] = {"ms": round(ms, 4), "tflops_counted": round(tf, 1),
-                      "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    legs["c5"] = {"ms": round(ms, 4), "tflops_counted": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                  "single_call_ms": round(ms_single, 4)}
     del x, o, lse, delta, dq, dk, dv
     torch.cuda.empty_cache()
     print(f"[bench] leg c5 {legs['c5']}", file=sys.stderr, flush=True)
