@@ -353,7 +353,8 @@ def psa_attn_fused(qkv, num_heads: int, key_dim: int, out=None, lse=None):
 def psa_attn_fused_backward(qkv, out, lse, d_out, num_heads: int, key_dim: int, d_qkv=None, delta=None):
     """Gradient of the PSA attention block with respect to qkv, from qkv, the
     block output `out` and its `lse` (psa_attn_fused with lse) and d_out.
-    Returns d_qkv [B, nh*4*kd, H, W] (key_dim 32, H*W <= 512; f16/bf16).
+    Returns d_qkv [B, nh*4*kd, H, W] (key_dim 32 with H*W <= 512, or key_dim
+    64 with H*W <= 128; f16/bf16).
     `delta` ([B*nh, H*W] float32) receives rowsum(out * d_out) per pixel."""
     _check("qkv", qkv)
     b, ch, h, w = qkv.shape

@@ -410,8 +410,10 @@ fa2_status psa_attn_fused_backward(fa2_dtype dt, const void *qkv, const void *ou
     fa2_status st = check_psa(fn, dt, batch, num_heads, key_dim, h, w);
     if (st != FA2_OK) return st;
     if (dt == FA2_F32) return fail(FA2_ERR_UNSUPPORTED, fn, "dtype must be F16 or BF16");
-    if (key_dim != 32) return fail(FA2_ERR_UNSUPPORTED, fn, "key_dim must be 32");
-    if ((int64_t)h * w > fa2mi::kPsaFusedBwdMaxPixels) return fail(FA2_ERR_UNSUPPORTED, fn, "h * w must be <= 512");
+    if (key_dim != 32 && key_dim != 64) return fail(FA2_ERR_UNSUPPORTED, fn, "key_dim must be 32 or 64");
+    if ((int64_t)h * w > fa2mi::psa_fused_bwd_max_pixels(key_dim))
+        return fail(FA2_ERR_UNSUPPORTED, fn,
+                    key_dim == 32 ? "h * w must be <= 512 at key_dim 32" : "h * w must be <= 128 at key_dim 64");
     REQUIRE_PTR(fn, qkv);
     REQUIRE_PTR(fn, out);
     REQUIRE_PTR(fn, d_out);

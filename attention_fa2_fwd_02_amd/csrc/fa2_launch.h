@@ -67,9 +67,10 @@ hipError_t launch_psa_merge_backward(int dt, const void *d_out, void *d_lo, void
                                      hipStream_t stream);
 hipError_t launch_psa_pack_backward(int dt, const void *d_packed, const void *d_qk_extra, void *d_qkv,
                                     const PsaShape &s, hipStream_t stream);
-// Fused block backward (key_dim 32, maps of at most kPsaFusedBwdMaxPixels
-// pixels): delta, then dQ, then dK/dV, all written into d_qkv.
-constexpr int kPsaFusedBwdMaxPixels = 512;
+// Fused block backward (key_dim 32 or 64, maps of at most
+// psa_fused_bwd_max_pixels(key_dim) pixels): delta, then dQ, then dK/dV, all
+// written into d_qkv. 0 for other key dims.
+constexpr int psa_fused_bwd_max_pixels(int key_dim) { return key_dim == 32 ? 512 : key_dim == 64 ? 128 : 0; }
 hipError_t launch_psa_fused_backward(int dt, const void *qkv, const void *out, const float *lse, const void *d_out,
                                      void *d_qkv, float *delta, const PsaShape &s, hipStream_t stream);
 hipError_t launch_psa_extract_v(int dt, const void *qkv, void *v, const PsaShape &s, hipStream_t stream);

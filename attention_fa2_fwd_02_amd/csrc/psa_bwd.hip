@@ -1,4 +1,5 @@
-// Fused backward of the C2PSA attention block for small maps (vision_rs
+// Fused backward of the C2PSA attention block for small maps (key_dim 32 up
+// to 512 pixels, key_dim 64 up to 128) (vision_rs
 // psa.rs: the block's backward hooks psa_merge_attn_backward,
 // psa_fa2_backward for both value halves, psa_pack_qkv_backward; vision-rs
 // flash_attn2.rs "Backward - dQ" and "Backward - dK / dV" for the algebra).
@@ -30,7 +31,6 @@ namespace fa2mi {
 
 namespace {
 
-constexpr int kPsaBwdKd = 32;    // key_dim handled by the fused backward
 constexpr int kPsaBwdBlock = 128; // pixels per workgroup block
 
 // delta[bh][n] = sum over the head's 2 kd output channels of out * d_out.
@@ -117,14 +117,18 @@ struct ChanStage {
 // Shared geometry: W = whole-map operand pair ([KD][CAP], [DV][CAP]), B =
 // 128-pixel block pair ([KD][128], [DV][128]). Row strides are an odd number
 // of 64-byte units (conflict-free transposing reads), rows shifted as above.
-template <int CAP>
+template <int KD_, int CAP>
 struct PsaBwdCfg {
-    static constexpr int KD = kPsaBwdKd, DV = 2 * KD, BR = kPsaBwdBlock, NT = 512;
+    static constexpr int KD = KD_, DV = 2 * KD, BR = kPsaBwdBlock, NT = 512;
     static constexpr int LDW = CAP + 32, LDB = BR + 32;
     static constexpr int W_K = KD * LDW, W_V = DV * LDW, B_K = KD * LDB, B_V = DV * LDB;
     static constexpr int NBH = CAP / 64;  // most 32-pixel blocks of one half of the map
     static constexpr int OPS_BYTES = 2 * (W_K + W_V + B_K + B_V);
     static_assert(OPS_BYTES + 2 * CAP * 4 <= 160 * 1024, "LDS");
+    // partial results exchanged through the operand space afterwards
+    // (floats per lane): dQ^T blocks; dK^T and dV^T blocks
+    static constexpr int XQ = 16 * (KD / 32), XKV = 16 * (KD / 32 + DV / 32);
+    static_assert(4 * 64 * XQ * 4 <= OPS_BYTES && 4 * 64 * XKV * 4 <= OPS_BYTES, "exchange");
 };
 
 }  // namespace
@@ -136,7 +140,7 @@ struct PsaBwdCfg {
 //   transposing reads, B from the block's Q^T / d_out^T likewise),
 //   dS^T = P^T (dP^T - delta), dQ^T += K^T dS^T (K^T rows, dS^T as B);
 // the two key halves' partial dQ^T are added through LDS.
-template <Dt DT, int CAP, bool ALIGNED>
+template <Dt DT, int KD_, int CAP, bool ALIGNED>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void psa_bwd_dq_kernel(
     const typename Traits<DT>::elem *__restrict__ qkv, const typename Traits<DT>::elem *__restrict__ d_out,
     const float *__restrict__ lse, const float *__restrict__ delta, typename Traits<DT>::elem *__restrict__ d_qkv,
@@ -144,8 +148,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     using Tr = Traits<DT>;
     using elem = typename Tr::elem;
     using frag = typename Tr::frag;
-    using C = PsaBwdCfg<CAP>;
+    using C = PsaBwdCfg<KD_, CAP>;
     constexpr int KD = C::KD, DV = C::DV, BR = C::BR, NT = C::NT, LDW = C::LDW, LDB = C::LDB;
+    constexpr int NCB = KD / 32;  // 32-channel blocks of dQ^T
     __shared__ __attribute__((aligned(16))) unsigned char lds_raw[C::OPS_BYTES];
     elem *Kt = reinterpret_cast<elem *>(lds_raw);
     elem *Vt = Kt + C::W_K;
@@ -190,7 +195,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int kb0 = ks ? nb_lo : 0;
     const int nb = ks ? nblk - nb_lo : nb_lo;
     const bool active = q0 + 32 * qs < hw && nb > 0;
-    f32x16 acc = zero16();
+    f32x16 acc[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc[cb] = zero16();
     if (active) {
         frag qf[KD / 16], df[DV / 16];
 #pragma unroll
@@ -212,33 +219,42 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 s[c] = p * (dp[c] - dl);
             }
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-                acc = Tr::mfma(ld_row_sh<DT>(Kt, LDW, col, kb0 + kb, t, h), c_to_frag<DT>(s, t), acc);
+            for (int t = 0; t < 2; ++t) {
+                const frag dsf = c_to_frag<DT>(s, t);
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    acc[cb] = Tr::mfma(ld_row_sh<DT>(Kt, LDW, 32 * cb + col, kb0 + kb, t, h), dsf, acc[cb]);
+            }
         }
     }
     __syncthreads();  // K^T / V^T no longer read: reuse the space
 
-    // key half 1 hands its partial dQ^T (registers c of lane (col, h)) to
-    // half 0 of the same query slice
-    float *xch = reinterpret_cast<float *>(lds_raw);  // [qs][64 lanes][16]
+    // key half 1 hands its partial dQ^T (registers c of lane (col, h) in
+    // each channel block) to half 0 of the same query slice
+    constexpr int XQ = C::XQ;
+    float *xch = reinterpret_cast<float *>(lds_raw);  // [qs][64 lanes][XQ]
     if (ks == 1) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-            *reinterpret_cast<float4 *>(xch + (qs * 64 + lane) * 16 + 4 * g) =
-                make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<float4 *>(xch + (qs * 64 + lane) * XQ + 16 * cb + 4 * g) =
+                    make_float4(acc[cb][4 * g], acc[cb][4 * g + 1], acc[cb][4 * g + 2], acc[cb][4 * g + 3]);
     }
     __syncthreads();
     if (ks == 0 && qrow < hw) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const float4 o = *reinterpret_cast<const float4 *>(xch + (qs * 64 + lane) * 16 + 4 * g);
-            const float ov[4] = {o.x, o.y, o.z, o.w};
+        for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int chn = crow(4 * g + i, h);  // Q channel
-                gbase[(int64_t)chn * hw + qrow] = static_cast<elem>((acc[4 * g + i] + ov[i]) * scale);
+            for (int g = 0; g < 4; ++g) {
+                const float4 o = *reinterpret_cast<const float4 *>(xch + (qs * 64 + lane) * XQ + 16 * cb + 4 * g);
+                const float ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int chn = 32 * cb + crow(4 * g + i, h);  // Q channel
+                    gbase[(int64_t)chn * hw + qrow] = static_cast<elem>((acc[cb][4 * g + i] + ov[i]) * scale);
+                }
             }
-        }
     }
 }
 
@@ -250,7 +266,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 //   P = exp2(S scale log2e - lse log2e), dS = P (dP - delta),
 //   dV^T += d_out^T P, dK^T += Q^T dS (A = rows of d_out^T / Q^T);
 // the two query halves' partial dK^T, dV^T are added through LDS.
-template <Dt DT, int CAP, bool ALIGNED>
+template <Dt DT, int KD_, int CAP, bool ALIGNED>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void psa_bwd_dkdv_kernel(
     const typename Traits<DT>::elem *__restrict__ qkv, const typename Traits<DT>::elem *__restrict__ d_out,
     const float *__restrict__ lse, const float *__restrict__ delta, typename Traits<DT>::elem *__restrict__ d_qkv,
@@ -258,8 +274,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     using Tr = Traits<DT>;
     using elem = typename Tr::elem;
     using frag = typename Tr::frag;
-    using C = PsaBwdCfg<CAP>;
+    using C = PsaBwdCfg<KD_, CAP>;
     constexpr int KD = C::KD, DV = C::DV, BR = C::BR, NT = C::NT, LDW = C::LDW, LDB = C::LDB;
+    constexpr int NCB = KD / 32;  // 32-channel blocks of dK^T
     __shared__ __attribute__((aligned(16))) unsigned char lds_raw[C::OPS_BYTES];
     __shared__ __attribute__((aligned(16))) float Ls[CAP];
     __shared__ __attribute__((aligned(16))) float Dl[CAP];
@@ -308,7 +325,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int qb0 = qh ? nb_lo : 0;
     const int nb = qh ? nblk - nb_lo : nb_lo;
     const bool active = k0 + 32 * ks < hw && nb > 0;
-    f32x16 accK = zero16(), accV[DV / 32];
+    f32x16 accK[NCB], accV[DV / 32];
+#pragma unroll
+    for (int i = 0; i < NCB; ++i) accK[i] = zero16();
 #pragma unroll
     for (int i = 0; i < DV / 32; ++i) accV[i] = zero16();
     if (active) {
@@ -349,24 +368,28 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                 for (int db = 0; db < DV / 32; ++db)
                     accV[db] = Tr::mfma(ld_row_sh<DT>(Dt_, LDW, 32 * db + col, qblock, t, h), pf, accV[db]);
-                accK = Tr::mfma(ld_row_sh<DT>(Qt, LDW, col, qblock, t, h), dsf, accK);
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    accK[cb] = Tr::mfma(ld_row_sh<DT>(Qt, LDW, 32 * cb + col, qblock, t, h), dsf, accK[cb]);
             }
         }
     }
     __syncthreads();  // Q^T / d_out^T no longer read: reuse the space
 
     // query half 1 hands its partial dK^T, dV^T to half 0 of the same key slice
-    constexpr int XF = 16 * (1 + DV / 32);  // floats per lane
+    constexpr int XF = C::XKV;  // floats per lane: dK^T blocks, then dV^T blocks
     float *xch = reinterpret_cast<float *>(lds_raw);  // [ks][64 lanes][XF]
     if (qh == 1) {
         float *dst = xch + (ks * 64 + lane) * XF;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            *reinterpret_cast<float4 *>(dst + 4 * g) =
-                make_float4(accK[4 * g], accK[4 * g + 1], accK[4 * g + 2], accK[4 * g + 3]);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+                *reinterpret_cast<float4 *>(dst + 16 * cb + 4 * g) =
+                    make_float4(accK[cb][4 * g], accK[cb][4 * g + 1], accK[cb][4 * g + 2], accK[cb][4 * g + 3]);
 #pragma unroll
             for (int db = 0; db < DV / 32; ++db)
-                *reinterpret_cast<float4 *>(dst + 16 * (1 + db) + 4 * g) =
+                *reinterpret_cast<float4 *>(dst + 16 * (NCB + db) + 4 * g) =
                     make_float4(accV[db][4 * g], accV[db][4 * g + 1], accV[db][4 * g + 2], accV[db][4 * g + 3]);
         }
     }
@@ -376,16 +399,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const float *src = xch + (ks * 64 + lane) * XF;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const float4 ok = *reinterpret_cast<const float4 *>(src + 4 * g);
-            const float okv[4] = {ok.x, ok.y, ok.z, ok.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int c = 4 * g + i;
-                gbase[(int64_t)(KD + crow(c, h)) * hw + krow] = static_cast<elem>((accK[c] + okv[i]) * scale);
+            for (int cb = 0; cb < NCB; ++cb) {
+                const float4 ok = *reinterpret_cast<const float4 *>(src + 16 * cb + 4 * g);
+                const float okv[4] = {ok.x, ok.y, ok.z, ok.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int c = 4 * g + i;
+                    gbase[(int64_t)(KD + 32 * cb + crow(c, h)) * hw + krow] =
+                        static_cast<elem>((accK[cb][c] + okv[i]) * scale);
+                }
             }
 #pragma unroll
             for (int db = 0; db < DV / 32; ++db) {
-                const float4 ov = *reinterpret_cast<const float4 *>(src + 16 * (1 + db) + 4 * g);
+                const float4 ov = *reinterpret_cast<const float4 *>(src + 16 * (NCB + db) + 4 * g);
                 const float ovv[4] = {ov.x, ov.y, ov.z, ov.w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -402,11 +429,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 namespace {
 
-template <Dt DT, int CAP, bool ALIGNED>
+template <Dt DT, int KD, int CAP, bool ALIGNED>
 hipError_t psa_bwd_launch(const void *qkv, const void *out, const float *lse, const void *d_out, void *d_qkv,
                           float *delta, const PsaShape &s, hipStream_t stream) {
     using elem = typename Traits<DT>::elem;
-    constexpr int KD = kPsaBwdKd, BR = kPsaBwdBlock;
+    constexpr int BR = kPsaBwdBlock;
     const int bhn = s.batch * s.num_heads;
     const int nblocks = (s.hw + BR - 1) / BR;
     const int grid = bhn * nblocks;
@@ -417,41 +444,52 @@ hipError_t psa_bwd_launch(const void *qkv, const void *out, const float *lse, co
                        (const elem *)d_out, delta, s.num_heads, s.hw, bph);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((psa_bwd_dq_kernel<DT, CAP, ALIGNED>), dim3(grid), dim3(512), 0, stream, (const elem *)qkv,
+    hipLaunchKernelGGL((psa_bwd_dq_kernel<DT, KD, CAP, ALIGNED>), dim3(grid), dim3(512), 0, stream, (const elem *)qkv,
                        (const elem *)d_out, lse, (const float *)delta, (elem *)d_qkv, s.num_heads, s.hw, nblocks,
                        grid, scale_log2, scale);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((psa_bwd_dkdv_kernel<DT, CAP, ALIGNED>), dim3(grid), dim3(512), 0, stream,
+    hipLaunchKernelGGL((psa_bwd_dkdv_kernel<DT, KD, CAP, ALIGNED>), dim3(grid), dim3(512), 0, stream,
                        (const elem *)qkv, (const elem *)d_out, lse, (const float *)delta, (elem *)d_qkv,
                        s.num_heads, s.hw, nblocks, grid, scale_log2, scale);
     return hipGetLastError();
 }
 
-template <Dt DT, int CAP>
+template <Dt DT, int KD, int CAP>
 hipError_t psa_bwd_aligned(const void *qkv, const void *out, const float *lse, const void *d_out, void *d_qkv,
                            float *delta, const PsaShape &s, hipStream_t stream) {
-    if (s.hw % 8 == 0) return psa_bwd_launch<DT, CAP, true>(qkv, out, lse, d_out, d_qkv, delta, s, stream);
-    return psa_bwd_launch<DT, CAP, false>(qkv, out, lse, d_out, d_qkv, delta, s, stream);
+    if (s.hw % 8 == 0) return psa_bwd_launch<DT, KD, CAP, true>(qkv, out, lse, d_out, d_qkv, delta, s, stream);
+    return psa_bwd_launch<DT, KD, CAP, false>(qkv, out, lse, d_out, d_qkv, delta, s, stream);
 }
 
-// Smallest whole-map capacity (64, 128, 256 or 512 pixels) that holds the map.
-template <Dt DT>
+// Smallest whole-map capacity that holds the map: 64, 128, 256 or 512
+// pixels at key_dim 32; 64 or 128 at key_dim 64 (the LDS holds the map's
+// Q^T, d_out^T or K^T, V^T plus a block of the other pair; capacities are
+// powers of two for the load mapping).
+template <Dt DT, int KD>
 hipError_t psa_bwd_dispatch(const void *qkv, const void *out, const float *lse, const void *d_out, void *d_qkv,
                             float *delta, const PsaShape &s, hipStream_t stream) {
-    if (s.hw <= 64) return psa_bwd_aligned<DT, 64>(qkv, out, lse, d_out, d_qkv, delta, s, stream);
-    if (s.hw <= 128) return psa_bwd_aligned<DT, 128>(qkv, out, lse, d_out, d_qkv, delta, s, stream);
-    if (s.hw <= 256) return psa_bwd_aligned<DT, 256>(qkv, out, lse, d_out, d_qkv, delta, s, stream);
-    return psa_bwd_aligned<DT, 512>(qkv, out, lse, d_out, d_qkv, delta, s, stream);
+    if (s.hw <= 64) return psa_bwd_aligned<DT, KD, 64>(qkv, out, lse, d_out, d_qkv, delta, s, stream);
+    if (s.hw <= 128) return psa_bwd_aligned<DT, KD, 128>(qkv, out, lse, d_out, d_qkv, delta, s, stream);
+    if constexpr (KD == 32) {
+        if (s.hw <= 256) return psa_bwd_aligned<DT, KD, 256>(qkv, out, lse, d_out, d_qkv, delta, s, stream);
+        return psa_bwd_aligned<DT, KD, 512>(qkv, out, lse, d_out, d_qkv, delta, s, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_psa_fused_backward(int dt, const void *qkv, const void *out, const float *lse, const void *d_out,
                                      void *d_qkv, float *delta, const PsaShape &s, hipStream_t stream) {
-    if (s.key_dim != kPsaBwdKd || s.hw > kPsaFusedBwdMaxPixels) return hipErrorInvalidValue;
-    if (dt == 1) return psa_bwd_dispatch<Dt::F16>(qkv, out, lse, d_out, d_qkv, delta, s, stream);
-    if (dt == 2) return psa_bwd_dispatch<Dt::BF16>(qkv, out, lse, d_out, d_qkv, delta, s, stream);
+    if (s.hw > psa_fused_bwd_max_pixels(s.key_dim)) return hipErrorInvalidValue;
+    if (s.key_dim == 32) {
+        if (dt == 1) return psa_bwd_dispatch<Dt::F16, 32>(qkv, out, lse, d_out, d_qkv, delta, s, stream);
+        if (dt == 2) return psa_bwd_dispatch<Dt::BF16, 32>(qkv, out, lse, d_out, d_qkv, delta, s, stream);
+    } else if (s.key_dim == 64) {
+        if (dt == 1) return psa_bwd_dispatch<Dt::F16, 64>(qkv, out, lse, d_out, d_qkv, delta, s, stream);
+        if (dt == 2) return psa_bwd_dispatch<Dt::BF16, 64>(qkv, out, lse, d_out, d_qkv, delta, s, stream);
+    }
     return hipErrorInvalidValue;
 }
 

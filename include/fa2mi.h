@@ -249,8 +249,9 @@ fa2_status psa_attn_fused(fa2_dtype dt, const void *qkv, void *out, float *lse,
  * (the sum of the two value halves' gradients of the pages' V-split, since
  * both halves share p). `delta` is a caller-owned float32 [batch*num_heads,
  * h*w] buffer (4-byte aligned) that receives delta. Three kernels, no
- * atomics, deterministic. dt F16 or BF16; key_dim 32; h*w <= 512, else
- * FA2_ERR_UNSUPPORTED (psa_block_backward's composition covers the rest).
+ * atomics, deterministic. dt F16 or BF16; key_dim 32 with h*w <= 512, or
+ * key_dim 64 with h*w <= 128, else FA2_ERR_UNSUPPORTED (psa_block_backward's
+ * composition covers the rest).
  * A V-extraction gradient is added afterwards with psa_extract_v_backward.
  */
 fa2_status psa_attn_fused_backward(fa2_dtype dt, const void *qkv, const void *out, const float *lse,

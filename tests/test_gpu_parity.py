@@ -841,17 +841,22 @@ PSA_FUSED_BWD_SHAPES = [(16, 4, 20, 20), (2, 3, 5, 7), (1, 2, 8, 8), (1, 2, 5, 1
                         (1, 1, 1, 257), (1, 2, 16, 28), (1, 1, 16, 32)]
 
 
+# key_dim 64: whole-map capacities 64 and 128, aligned and not
+PSA_FUSED_BWD_CASES = [(32,) + sh for sh in PSA_FUSED_BWD_SHAPES] + [
+    (64, 2, 1, 5, 7), (64, 1, 3, 8, 8), (64, 2, 2, 9, 9), (64, 3, 2, 4, 30), (64, 1, 2, 8, 16)]
+
+
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
-@pytest.mark.parametrize("b,nh,h,w", PSA_FUSED_BWD_SHAPES, ids=lambda v: str(v))
-def test_psa_attn_fused_backward(dt, b, nh, h, w):
+@pytest.mark.parametrize("kd,b,nh,h,w", PSA_FUSED_BWD_CASES, ids=lambda v: str(v))
+def test_psa_attn_fused_backward(dt, kd, b, nh, h, w):
     """The fused block backward (three kernels, NCHW in and out) against the
-    oracle's fp64 chain rule of the block; maps from 35 to 512 pixels cover
-    every whole-map capacity (64, 128, 256, 512) with and without 16-byte
-    aligned rows. Also: delta is rowsum(out * d_out), and a second call gives
-    the same bits."""
-    kd = 32
+    oracle's fp64 chain rule of the block; at key_dim 32 maps from 35 to 512
+    pixels cover every whole-map capacity (64, 128, 256, 512), at key_dim 64
+    maps from 35 to 128 pixels the capacities 64 and 128, each with and
+    without 16-byte aligned rows. Also: delta is rowsum(out * d_out), and a
+    second call gives the same bits."""
     dtype = DTYPES[dt]
-    case = f"psa fused bwd {dt} b={b} nh={nh} h={h} w={w}"
+    case = f"psa fused bwd {dt} kd={kd} b={b} nh={nh} h={h} w={w}"
     print(case, flush=True)
     wl = workloads.PsaWorkload("case", b, nh, kd, h, w, dt, seed=71 + h * w)
     qkv = workloads.psa_inputs(wl, device=DEV)
@@ -893,8 +898,15 @@ def test_psa_attn_fused_backward_rejects_unsupported():
     qkv = torch.zeros(1, 4 * 64, 4, 4, dtype=torch.float16, device=DEV)
     out = torch.zeros(1, 2 * 64, 4, 4, dtype=torch.float16, device=DEV)
     lse = torch.zeros(1, 16, dtype=torch.float32, device=DEV)
-    with pytest.raises(fa2.Fa2Error, match="key_dim must be 32"):
-        fa2.psa_attn_fused_backward(qkv, out, lse, out, 1, 64)
+    qkv128 = torch.zeros(1, 4 * 128, 4, 4, dtype=torch.float16, device=DEV)
+    out128 = torch.zeros(1, 2 * 128, 4, 4, dtype=torch.float16, device=DEV)
+    with pytest.raises(fa2.Fa2Error, match="key_dim must be 32 or 64"):
+        fa2.psa_attn_fused_backward(qkv128, out128, lse, out128, 1, 128)
+    qkv64 = torch.zeros(1, 4 * 64, 1, 129, dtype=torch.float16, device=DEV)
+    out64 = torch.zeros(1, 2 * 64, 1, 129, dtype=torch.float16, device=DEV)
+    lse64 = torch.zeros(1, 129, dtype=torch.float32, device=DEV)
+    with pytest.raises(fa2.Fa2Error, match="128 at key_dim 64"):
+        fa2.psa_attn_fused_backward(qkv64, out64, lse64, out64, 1, 64)
     qkv = torch.zeros(1, 4 * 32, 1, 513, dtype=torch.float16, device=DEV)
     out = torch.zeros(1, 2 * 32, 1, 513, dtype=torch.float16, device=DEV)
     lse = torch.zeros(1, 513, dtype=torch.float32, device=DEV)
