@@ -101,8 +101,12 @@ def test_bwd_and_psa_reject_invalid_arguments():
     assert lib.psa_extract_v_backward(2, A, A, 16, 4, 32, -1, 20, None) == INVALID
     fb = lib.psa_attn_fused_backward
     assert fb(0, A, A, A, A, A, A, 16, 4, 32, 20, 20, None) == UNSUPPORTED      # f32
-    assert fb(1, A, A, A, A, A, A, 16, 4, 64, 20, 20, None) == UNSUPPORTED      # key_dim 64
-    assert fb(1, A, A, A, A, A, A, 16, 4, 32, 16, 33, None) == UNSUPPORTED      # 528 pixels
+    assert fb(1, A, A, A, A, A, A, 16, 4, 128, 4, 4, None) == UNSUPPORTED      # key_dim 128
+    assert b"key_dim must be 32 or 64" in lib.fa2_last_error()
+    assert fb(1, A, A, A, A, A, A, 16, 4, 64, 20, 20, None) == UNSUPPORTED      # key_dim 64, 400 pixels
+    assert b"<= 128 at key_dim 64" in lib.fa2_last_error()
+    assert fb(1, A, A, A, A, A, A, 16, 4, 32, 16, 33, None) == UNSUPPORTED      # key_dim 32, 528 pixels
+    assert b"<= 512 at key_dim 32" in lib.fa2_last_error()
     assert fb(1, A, A, None, A, A, A, 16, 4, 32, 20, 20, None) == INVALID       # lse
     assert fb(2, A, A, A, A, A, A + 2, 16, 4, 32, 20, 20, None) == INVALID      # delta misaligned
     assert fb(2, A, MIS, A, A, A, A, 16, 4, 32, 20, 20, None) == INVALID        # out misaligned
