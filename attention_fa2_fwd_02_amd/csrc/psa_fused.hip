@@ -296,8 +296,12 @@ struct PsaSmallCfg {
     static constexpr int LDX = CPS + 4;
     static constexpr int XCH_FLOATS = NW * (KS - 1) * 32 * LDX + NW * 2 * 32;
     static constexpr int MAIN_BYTES = 2 * (KT_SZ + VT_SZ + QT_SZ);
-    static constexpr int LDS_BYTES = MAIN_BYTES > 4 * XCH_FLOATS ? MAIN_BYTES : 4 * XCH_FLOATS;
-    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+    // the exchange sits past the operands when both fit (no barrier before
+    // it), else it reuses their space
+    static constexpr bool SEPX = MAIN_BYTES + 4 * XCH_FLOATS <= 160 * 1024;
+    static constexpr int LDS_BYTES = SEPX ? MAIN_BYTES + 4 * XCH_FLOATS
+                                          : (MAIN_BYTES > 4 * XCH_FLOATS ? MAIN_BYTES : 4 * XCH_FLOATS);
+    static_assert(LDS_BYTES <= 160 * 1024 && MAIN_BYTES % 16 == 0, "LDS");
     static_assert(CPS == 16 || CPS == 32 || CPS == 64, "channel slices of whole C-block halves");
 };
 
@@ -462,7 +466,7 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, KS
         }
     }
     const float l_slice = xhalf_sum(l_run);
-    __syncthreads();  // K^T / V^T no longer read: reuse the space
+    if constexpr (!C::SEPX) __syncthreads();  // K^T / V^T no longer read: reuse the space
 
     // Merge the KS slices. Wave (qs, ks) finishes channels [ks CPS, (ks+1)
     // CPS) and hands every other slice's channels to that slice's wave. A
@@ -473,7 +477,7 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, KS
     // [source wave][other-slice index][query][LDX] floats, then m and l.
     // NSB whole blocks per slice when CPS >= 32.
     constexpr int CPS = C::CPS, LDX = C::LDX, RN = CPS >= 32 ? 16 : 8, NSB = CPS >= 32 ? CPS / 32 : 1;
-    float *xch = reinterpret_cast<float *>(lds_raw);
+    float *xch = reinterpret_cast<float *>(lds_raw + (C::SEPX ? C::MAIN_BYTES : 0));
     float *ml = xch + C::NW * (KS - 1) * 32 * LDX;  // [wave][2][32]
     constexpr auto slice_db = [](int j) { return (j * CPS) / 32; };
     constexpr auto slice_rl = [](int j) { return CPS >= 32 ? 0 : ((j * CPS) % 32) / 2; };
